@@ -1,0 +1,39 @@
+"""CPU oracle for the QLoRA NF4 linear layer.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
+definition that the HIP library is checked against. Only the test suite, the
+smoke check and the CPU-baseline leg of the benchmark may import it; the
+product path never does. It shares no code, tables or constants with the HIP
+library under ``bit_quantized_finetuning_quantize_amd/``.
+
+Sources (the pages are cited by address, title and section):
+
+* [P1] ai360xpert.com/papers/qlora, "QLoRA"
+* [P2] crackai.dev/papers/qlora, "QLoRA: Efficient Finetuning of Quantized LLMs"
+* [P3] narrativegoldmine.com/notes/pages/QLoRA, "QLoRA"
+* [P4] ozercemkelahmet.com/tools/qlora, "QLoRA"
+* [P5] fanfani.net/articles/qlora, "QLoRA"
+
+Pinning status of each function is stated in its module docstring.
+"""
+
+from .nf4 import (  # noqa: F401
+    BLOCK,
+    GROUP,
+    P_MAX,
+    codebook,
+    codebook_fp64,
+    level8,
+    nearest_level,
+    quantize,
+    dequantize,
+    unpack_codes,
+    pack_codes,
+    num_blocks,
+    num_groups,
+    codes_bytes,
+    store_bytes,
+    bits_per_param,
+)
+from .bf16 import bf16_round, bf16_bits_to_f32, f32_to_bf16_bits  # noqa: F401
+from .linear import linear_fwd, linear_bwd  # noqa: F401
