@@ -1,0 +1,148 @@
+"""Thin Python binding over the C ABI (argument marshalling only).
+
+Every computation runs in libqlora.so on the caller's current HIP stream;
+torch is used only to hold device memory and to name the stream. Function
+names match include/qlora.h.
+"""
+
+import ctypes
+
+import torch
+
+from ._lib import LIB
+
+BLOCK = 64
+GROUP = 256
+
+
+class QloraError(RuntimeError):
+    pass
+
+
+def _check(status):
+    if status != 0:
+        msg = LIB.qlora_status_string(status).decode()
+        hip = LIB.qlora_last_hip_error() if status == -4 else 0
+        raise QloraError(f"qlora status {status}: {msg}" + (f" (hipError {hip})" if hip else ""))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise QloraError(f"{name} must be a contiguous {dtype} tensor on the GPU")
+
+
+def qlora_nf4_codes_bytes(numel):
+    return int(LIB.qlora_nf4_codes_bytes(numel))
+
+
+def qlora_nf4_num_blocks(numel):
+    return int(LIB.qlora_nf4_num_blocks(numel))
+
+
+def qlora_nf4_num_groups(numel):
+    return int(LIB.qlora_nf4_num_groups(numel))
+
+
+def qlora_nf4_codebook():
+    buf = (ctypes.c_float * 16)()
+    LIB.qlora_nf4_codebook(ctypes.cast(buf, ctypes.c_void_p))
+    return list(buf)
+
+
+class Nf4Store:
+    """The three device buffers of one NF4 tensor (owned by torch)."""
+
+    def __init__(self, codes, absmax_q, absmax_s2, numel, shape=None):
+        self.codes, self.absmax_q, self.absmax_s2 = codes, absmax_q, absmax_s2
+        self.numel = int(numel)
+        self.shape = tuple(shape) if shape is not None else (self.numel,)
+
+    def nbytes(self):
+        return self.codes.numel() + self.absmax_q.numel() + 4 * self.absmax_s2.numel()
+
+
+def empty_store(numel, device, shape=None):
+    codes = torch.empty(qlora_nf4_codes_bytes(numel), dtype=torch.uint8, device=device)
+    q8 = torch.empty(qlora_nf4_num_blocks(numel), dtype=torch.uint8, device=device)
+    s2 = torch.empty(qlora_nf4_num_groups(numel), dtype=torch.float32, device=device)
+    return Nf4Store(codes, q8, s2, numel, shape)
+
+
+def qlora_nf4_quantize(w, out=None):
+    """Quantize a bf16 tensor (any shape, flattened row-major)."""
+    _need(w, torch.bfloat16, "w")
+    st = out if out is not None else empty_store(w.numel(), w.device, w.shape)
+    _check(LIB.qlora_nf4_quantize(_ptr(w), w.numel(), _ptr(st.codes), _ptr(st.absmax_q),
+                                  _ptr(st.absmax_s2), _stream()))
+    return st
+
+
+def qlora_nf4_dequantize(st, out=None):
+    out = out if out is not None else torch.empty(st.numel, dtype=torch.float32,
+                                                  device=st.codes.device)
+    _check(LIB.qlora_nf4_dequantize(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2),
+                                    st.numel, _ptr(out), _stream()))
+    return out
+
+
+def qlora_nf4_dequantize_bf16(st, out=None):
+    out = out if out is not None else torch.empty(st.numel, dtype=torch.bfloat16,
+                                                  device=st.codes.device)
+    _check(LIB.qlora_nf4_dequantize_bf16(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2),
+                                         st.numel, _ptr(out), _stream()))
+    return out
+
+
+def qlora_linear_workspace_bytes(M, N, K, r):
+    return int(LIB.qlora_linear_workspace_bytes(M, N, K, r))
+
+
+def workspace(M, N, K, r, device):
+    n = qlora_linear_workspace_bytes(M, N, K, r)
+    if n == 0:
+        raise QloraError(f"unsupported linear shape M={M} N={N} K={K} r={r}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def qlora_linear_fwd(X, W, A, B, scale, want_T=True, Y=None, T=None, ws=None):
+    """Y = X bf16(W')^T + scale (X A) B; returns (Y, T) with T fp32 or None."""
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[1]
+    for t, name in ((X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, name)
+    Y = Y if Y is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    if want_T and T is None:
+        T = torch.empty(M, r, dtype=torch.float32, device=X.device)
+    ws = ws if ws is not None else workspace(M, N, K, r, X.device)
+    _check(LIB.qlora_linear_fwd(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q), _ptr(W.absmax_s2),
+                                _ptr(A), _ptr(B), M, N, K, r, float(scale), _ptr(Y),
+                                _ptr(T) if want_T else None, _ptr(ws), ws.numel(), _stream()))
+    return Y, (T if want_T else None)
+
+
+def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, dB=None, ws=None):
+    """Returns (dX or None, dA fp32 [K x r], dB fp32 [r x N])."""
+    M, N = dY.shape
+    K = X.shape[1]
+    r = A.shape[1]
+    for t, name in ((dY, "dY"), (X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, name)
+    if want_dX and dX is None:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    dA = dA if dA is not None else torch.empty(K, r, dtype=torch.float32, device=X.device)
+    dB = dB if dB is not None else torch.empty(r, N, dtype=torch.float32, device=X.device)
+    ws = ws if ws is not None else workspace(M, N, K, r, X.device)
+    _check(LIB.qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(T), _ptr(W.codes), _ptr(W.absmax_q),
+                                _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r, float(scale),
+                                _ptr(dX) if want_dX else None, _ptr(dA), _ptr(dB), _ptr(ws),
+                                ws.numel(), _stream()))
+    return (dX if want_dX else None), dA, dB

@@ -1,0 +1,148 @@
+// C ABI of the library: argument validation, dispatch, status codes.
+// Every check runs before anything is enqueued; a rejected call has no side
+// effects and makes no HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/qlora.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QLORA_OK;
+  g_last_hip_error = (int)e;
+  return QLORA_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxGroups = 0x7fffffffLL;  // grid limit of the quantize launch
+
+int check_store(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2) {
+  if (!codes || !absmax_q || !absmax_s2) return QLORA_ERR_INVALID_ARG;
+  if (!aligned(codes, 16) || !aligned(absmax_s2, 4)) return QLORA_ERR_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+int check_linear_shape(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M <= 0 || N <= 0 || K <= 0) return QLORA_ERR_INVALID_ARG;
+  if (K % QLORA_NF4_BLOCK != 0 || N % QLORA_NF4_BLOCK != 0) return QLORA_ERR_UNSUPPORTED;
+  if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return QLORA_ERR_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t qlora_nf4_codes_bytes(int64_t numel) { return numel < 0 ? -1 : (numel + 1) / 2; }
+int64_t qlora_nf4_num_blocks(int64_t numel) {
+  return numel < 0 ? -1 : (numel + QLORA_NF4_BLOCK - 1) / QLORA_NF4_BLOCK;
+}
+int64_t qlora_nf4_num_groups(int64_t numel) {
+  return numel < 0 ? -1 : (qlora_nf4_num_blocks(numel) + QLORA_NF4_GROUP - 1) / QLORA_NF4_GROUP;
+}
+
+void qlora_nf4_codebook(float* levels) {
+  if (!levels) return;
+  std::memcpy(levels, qlora::kNF4, sizeof(qlora::kNF4));
+}
+
+int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
+                       float* absmax_s2, void* stream) {
+  if (!w || numel <= 0) return QLORA_ERR_INVALID_ARG;
+  if (!codes || !absmax_q || !absmax_s2) return QLORA_ERR_INVALID_ARG;
+  if (!aligned(w, 2) || !aligned(codes, 4) || !aligned(absmax_s2, 4)) return QLORA_ERR_UNSUPPORTED;
+  if (qlora_nf4_num_groups(numel) > kMaxGroups) return QLORA_ERR_UNSUPPORTED;
+  return hip_status(qlora::launch_nf4_quantize(w, numel, codes, absmax_q, absmax_s2,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+static int dequant_common(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                          int64_t numel, void* out, bool bf16, void* stream) {
+  if (!codes || !absmax_q || !absmax_s2 || !out || numel <= 0) return QLORA_ERR_INVALID_ARG;
+  if (!aligned(codes, 4) || !aligned(absmax_s2, 4) || !aligned(out, 16)) return QLORA_ERR_UNSUPPORTED;
+  return hip_status(qlora::launch_nf4_dequantize(codes, absmax_q, absmax_s2, numel, out, bf16,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qlora_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                         int64_t numel, float* out, void* stream) {
+  return dequant_common(codes, absmax_q, absmax_s2, numel, out, false, stream);
+}
+
+int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
+                              const float* absmax_s2, int64_t numel, uint16_t* out,
+                              void* stream) {
+  return dequant_common(codes, absmax_q, absmax_s2, numel, out, true, stream);
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (check_linear_shape(M, N, K, r) != QLORA_OK) return 0;
+  return qlora::linear_workspace_bytes(M, N, K, r);
+}
+
+int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                     const float* absmax_s2, const uint16_t* A, const uint16_t* B, int64_t M,
+                     int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y, float* T_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  int st = check_store(codes, absmax_q, absmax_s2);
+  if (st != QLORA_OK) return st;
+  st = check_linear_shape(M, N, K, r);
+  if (st != QLORA_OK) return st;
+  if (!aligned(X, 16) || !aligned(B, 16) || !aligned(A, 2) || !aligned(Y, 2) ||
+      (T_out && !aligned(T_out, 4)))
+    return QLORA_ERR_UNSUPPORTED;
+  const size_t need = qlora::linear_workspace_bytes(M, N, K, r);
+  if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (M <= qlora::kGemvMaxM)
+    return hip_status(qlora::launch_fwd_gemv(X, W, A, B, (int)M, N, K, r, scale, Y, T_out, ws, s));
+  return hip_status(qlora::launch_fwd_gemm(X, W, A, B, M, N, K, r, scale, Y, T_out, ws, s));
+}
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, const uint8_t* codes,
+                     const uint8_t* absmax_q, const float* absmax_s2, const uint16_t* A,
+                     const uint16_t* B, int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                     uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!dY || !X || !A || !B || !dA || !dB) return QLORA_ERR_INVALID_ARG;
+  int st = check_store(codes, absmax_q, absmax_s2);
+  if (st != QLORA_OK) return st;
+  st = check_linear_shape(M, N, K, r);
+  if (st != QLORA_OK) return st;
+  if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(B, 16) || !aligned(A, 2) ||
+      (T && !aligned(T, 4)) || (dX && !aligned(dX, 2)) || !aligned(dA, 4) || !aligned(dB, 4))
+    return QLORA_ERR_UNSUPPORTED;
+  const size_t need = qlora::linear_workspace_bytes(M, N, K, r);
+  if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  return hip_status(qlora::launch_bwd(dY, X, T, W, A, B, M, N, K, r, scale, dX, dA, dB, ws,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported shape, rank or alignment";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

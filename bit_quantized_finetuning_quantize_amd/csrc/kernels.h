@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Launchers enqueue on `stream`, never synchronize, and return the launch
+// status. Shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+struct Nf4Weight {
+  const uint8_t* codes;
+  const uint8_t* absmax_q;
+  const float* absmax_s2;
+};
+
+hipError_t launch_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
+                               uint8_t* absmax_q, float* absmax_s2,
+                               hipStream_t stream);
+
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
+                                 const float* absmax_s2, int64_t numel, void* out,
+                                 bool bf16, hipStream_t stream);
+
+// ---- linear layer -----------------------------------------------------------
+
+// Workspace carve-up for the forward and backward of one linear call.
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+
+// Small-M forward (M <= kGemvMaxM): split-K GEMV with the LoRA epilogue.
+constexpr int kGemvMaxM = 16;
+int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K);
+hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A,
+                           const uint16_t* B, int M, int64_t N, int64_t K, int r,
+                           float scale, uint16_t* Y, float* T_out, void* ws,
+                           hipStream_t stream);
+
+// Large-M forward: T = X A, then Y = [X | s T] [W' | B^T]^T on MFMA tiles.
+hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
+                           const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                           int r, float scale, uint16_t* Y, float* T_out, void* ws,
+                           hipStream_t stream);
+
+// Backward: G = dY B^T, dX = [dY | s G] [W' ; A^T], dA = s X^T G, dB = s T^T dY.
+hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
+                      Nf4Weight W, const uint16_t* A, const uint16_t* B,
+                      int64_t M, int64_t N, int64_t K, int r, float scale,
+                      uint16_t* dX, float* dA, float* dB, void* ws,
+                      hipStream_t stream);
+
+}  // namespace qlora

@@ -1,0 +1,218 @@
+// NF4 quantization (with double quantization) and dequantization kernels.
+//
+// Quantization follows ozercemkelahmet.com "QLoRA", How it works, Step 1
+// (blocks of 64 scaled by their largest magnitude, each value replaced by
+// the nearest of 16 NormalFloat levels), Step 2 (one constant per block) and
+// Step 3 (the constants quantized again to 8 bits in groups with their own
+// second-level constants); ai360xpert.com "QLoRA", How It Works item 2
+// (32-bit constants to 8-bit).
+//
+// Layout of one launch: one workgroup per group of 256 blocks (16384 values).
+// Within a workgroup, eight consecutive lanes own one block (8 values each,
+// one 16-byte load), so every load instruction of a wave reads 1 KiB of
+// contiguous HBM and a block maximum is a three-step xor shuffle. A
+// workgroup walks its group in 8 rounds of 32 blocks, keeping the values in
+// registers, so each input byte is read once.
+#include "common.h"
+#include "kernels.h"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kRounds = kGroup * kBlock / (kQuantThreads * 8);  // 8
+
+__device__ __forceinline__ uint32_t nf4_index(float n) {
+  uint32_t q = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) q += (n > kThr.t[j]) ? 1u : 0u;
+  return q;
+}
+
+template <bool kVec>
+__global__ void __launch_bounds__(kQuantThreads)
+nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
+                    uint8_t* __restrict__ codes, uint8_t* __restrict__ absmax_q,
+                    float* __restrict__ absmax_s2) {
+#pragma clang fp contract(off)
+  __shared__ float s_blockmax[kGroup];
+  __shared__ float s_wavemax[kQuantThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int64_t group = blockIdx.x;
+  const int64_t gbase = group * (int64_t)(kGroup * kBlock);
+  const int64_t nbytes = (numel + 1) / 2;
+
+  uint32_t vals[kRounds][4];  // 8 bf16 per round
+  float cmax[kRounds];
+
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t e0 = gbase + (int64_t)r * (kQuantThreads * 8) + tid * 8;
+    if (kVec && e0 + 8 <= numel) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(w + e0);
+      vals[r][0] = v.x; vals[r][1] = v.y; vals[r][2] = v.z; vals[r][3] = v.w;
+    } else {
+      uint16_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (e0 + i < numel) ? w[e0 + i] : (uint16_t)0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vals[r][i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = fmaxf(m, fabsf(bf16_lo(vals[r][i])));
+      m = fmaxf(m, fabsf(bf16_hi(vals[r][i])));
+    }
+    // the 8 lanes of a block are consecutive and aligned to 8 inside a wave
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    cmax[r] = m;
+    if ((tid & 7) == 0) s_blockmax[r * (kQuantThreads / 8) + tid / 8] = m;
+  }
+  __syncthreads();
+
+  // second level: group maximum over the 256 block constants
+  float gm = s_blockmax[tid];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+  if ((tid & 63) == 0) s_wavemax[tid / 64] = gm;
+  __syncthreads();
+  const float s2 = fmaxf(fmaxf(s_wavemax[0], s_wavemax[1]),
+                         fmaxf(s_wavemax[2], s_wavemax[3]));
+
+  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
+  {
+    const int64_t b = group * kGroup + tid;
+    if (b < nblocks) {
+      uint32_t q8 = 0;
+      if (s2 > 0.0f) {
+        const float ratio = s_blockmax[tid] / s2;   // IEEE division
+        const float scaled = ratio * 255.0f;
+        q8 = (uint32_t)fminf(fmaxf(rintf(scaled), 0.0f), 255.0f);  // half-even
+      }
+      absmax_q[b] = (uint8_t)q8;
+    }
+    if (tid == 0) absmax_s2[group] = s2;
+  }
+
+  // first level: codes against the exact float32 block maximum
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t e0 = gbase + (int64_t)r * (kQuantThreads * 8) + tid * 8;
+    if (e0 >= numel) continue;
+    const float c = cmax[r];
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_lo(vals[r][i]);
+      const float b = bf16_hi(vals[r][i]);
+      const uint32_t qa = (c > 0.0f) ? nf4_index(a / c) : 7u;
+      const uint32_t qb = (c > 0.0f) ? nf4_index(b / c) : 7u;
+      word |= (qa | (qb << 4)) << (8 * i);
+    }
+    const int64_t byte0 = e0 / 2;
+    if (byte0 + 4 <= nbytes) {
+      *reinterpret_cast<uint32_t*>(codes + byte0) = word;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (byte0 + i < nbytes) codes[byte0 + i] = (uint8_t)(word >> (8 * i));
+    }
+  }
+}
+
+// Dequantization: one lane per 8 values (one 32-bit code word).
+template <bool kBf16>
+__global__ void __launch_bounds__(256)
+nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
+                      const uint8_t* __restrict__ absmax_q,
+                      const float* __restrict__ absmax_s2, int64_t numel,
+                      void* __restrict__ out) {
+#pragma clang fp contract(off)
+  __shared__ float s_lv[16];
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const int64_t nwords = (numel + 7) / 8;
+  const int64_t nbytes = (numel + 1) / 2;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nwords;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = i * 8;
+    uint32_t word;
+    if (i * 4 + 4 <= nbytes) {
+      word = *reinterpret_cast<const uint32_t*>(codes + i * 4);
+    } else {
+      word = 0;
+      for (int j = 0; j < 4; ++j)
+        if (i * 4 + j < nbytes) word |= (uint32_t)codes[i * 4 + j] << (8 * j);
+    }
+    const int64_t b = e0 / kBlock;
+    const float cs = block_scale(absmax_q[b], absmax_s2[b / kGroup]);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = s_lv[(word >> (4 * j)) & 15u] * cs;
+    if (kBf16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      if (e0 + 8 <= numel) {
+        u32x4 p;
+        p.x = pack_bf16x2(v[0], v[1]);
+        p.y = pack_bf16x2(v[2], v[3]);
+        p.z = pack_bf16x2(v[4], v[5]);
+        p.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<u32x4*>(o + e0) = p;
+      } else {
+        for (int j = 0; j < 8; ++j)
+          if (e0 + j < numel)
+            o[e0 + j] = (uint16_t)(pack_bf16x2(v[j], 0.0f) & 0xffffu);
+      }
+    } else {
+      float* o = reinterpret_cast<float*>(out);
+      if (e0 + 8 <= numel) {
+        floatx4 a = {v[0], v[1], v[2], v[3]};
+        floatx4 c = {v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<floatx4*>(o + e0) = a;
+        *reinterpret_cast<floatx4*>(o + e0 + 4) = c;
+      } else {
+        for (int j = 0; j < 8; ++j)
+          if (e0 + j < numel) o[e0 + j] = v[j];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
+                               uint8_t* absmax_q, float* absmax_s2,
+                               hipStream_t stream) {
+  const int64_t ngroups = (numel + (int64_t)kGroup * kBlock - 1) / ((int64_t)kGroup * kBlock);
+  const bool vec = (reinterpret_cast<uintptr_t>(w) % 16) == 0;
+  dim3 grid((unsigned)ngroups), block(kQuantThreads);
+  if (vec)
+    hipLaunchKernelGGL(nf4_quantize_kernel<true>, grid, block, 0, stream, w, numel,
+                       codes, absmax_q, absmax_s2);
+  else
+    hipLaunchKernelGGL(nf4_quantize_kernel<false>, grid, block, 0, stream, w, numel,
+                       codes, absmax_q, absmax_s2);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
+                                 const float* absmax_s2, int64_t numel, void* out,
+                                 bool bf16, hipStream_t stream) {
+  const int64_t nwords = (numel + 7) / 8;
+  int64_t blocks = (nwords + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (bf16)
+    hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, codes, absmax_q, absmax_s2, numel, out);
+  else
+    hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, codes, absmax_q, absmax_s2, numel, out);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

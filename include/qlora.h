@@ -1,0 +1,197 @@
+/*
+ * qlora.h — C ABI of the MI355X (gfx950) NF4 linear layer with a LoRA adapter.
+ *
+ * The library implements the frozen 4-bit linear layer of QLoRA finetuning:
+ * blockwise NormalFloat-4 quantization with double quantization of the block
+ * constants, the forward product with dequantization fused into a bfloat16
+ * matrix product, and the backward pass that returns gradients for the input
+ * and the two adapter matrices only.
+ *
+ * Sources (page address, title, section):
+ *   ozercemkelahmet.com/tools/qlora "QLoRA", How it works, Steps 1-6, and
+ *     "A worked example";
+ *   crackai.dev/papers/qlora "QLoRA: Efficient Finetuning of Quantized LLMs",
+ *     How It Works items 1-2 and Training Flow;
+ *   ai360xpert.com/papers/qlora "QLoRA", How It Works items 1-2;
+ *   fanfani.net/articles/qlora "QLoRA", "The crucial split: store in four
+ *     bits, compute in sixteen".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument that names a tensor is a DEVICE pointer (memory of
+ *   the GPU that is current on the calling thread) unless stated otherwise.
+ *   The caller owns all memory; the library never allocates, frees or
+ *   synchronizes, and keeps no state between calls.
+ * - bfloat16 tensors are passed as uint16_t bit patterns; float tensors are
+ *   IEEE binary32. All matrices are dense, row-major, contiguous.
+ * - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on
+ *   it and the call returns without waiting.
+ * - Return value: QLORA_OK (0) or a negative status. Arguments are validated
+ *   before anything is enqueued; a failed validation has no side effects.
+ *   QLORA_ERR_HIP means a launch failed; qlora_last_hip_error() then returns
+ *   the hipError_t of the calling thread's last failure. Nothing prints,
+ *   throws or aborts.
+ * - Calls that share a workspace buffer must not overlap in time (same
+ *   stream, or caller-side ordering).
+ *
+ * The NF4 store
+ * -------------
+ * A tensor of `numel` values (flat, row-major) is stored in three buffers:
+ *   codes     uint8 [qlora_nf4_codes_bytes(numel) = ceil(numel/2)]
+ *             4-bit level indices; element 2i in the low nibble of byte i,
+ *             element 2i+1 in the high nibble; an odd tail leaves the last
+ *             high nibble 0.
+ *   absmax_q  uint8 [qlora_nf4_num_blocks(numel) = ceil(numel/64)]
+ *             8-bit code of each block's absolute maximum.
+ *   absmax_s2 float [qlora_nf4_num_groups(numel) = ceil(nblocks/256)]
+ *             second-level constant (maximum block constant) of each group
+ *             of 256 consecutive blocks.
+ * Dequantized value of element i (block b = i/64, group g = b/256):
+ *   c'  = fl32( fl32(absmax_q[b] / 255) * absmax_s2[g] )
+ *   w'  = fl32( NF4[code_i] * c' )
+ * and the compute weight is bf16(w'), rounded to nearest even.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1, /* null required pointer, bad size, numel mismatch */
+  QLORA_ERR_UNSUPPORTED = -2, /* K % 64 != 0, r outside [1, 256], misaligned pointer */
+  QLORA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  QLORA_ERR_HIP = -4          /* a HIP launch failed; see qlora_last_hip_error() */
+};
+
+#define QLORA_NF4_BLOCK 64
+#define QLORA_NF4_GROUP 256
+#define QLORA_MAX_RANK 256
+
+/* ---- sizes of the NF4 store (host functions, no GPU work) ---------------- */
+
+/* ceil(numel / 2); -1 if numel < 0. */
+int64_t qlora_nf4_codes_bytes(int64_t numel);
+/* ceil(numel / 64); -1 if numel < 0. */
+int64_t qlora_nf4_num_blocks(int64_t numel);
+/* ceil(ceil(numel / 64) / 256); -1 if numel < 0. */
+int64_t qlora_nf4_num_groups(int64_t numel);
+
+/* The 16 NF4 levels as used by the kernels, ascending (host copy).
+ * They are the float32 roundings of standard-normal quantiles at equal
+ * probability steps within each half, scaled so the endpoints are -1 and +1
+ * with an exact 0 (crackai.dev "QLoRA: Efficient Finetuning of Quantized
+ * LLMs", How It Works item 1; ozercemkelahmet.com "QLoRA", Why NormalFloat).
+ * `levels` is a HOST pointer to 16 floats. */
+void qlora_nf4_codebook(float* levels);
+
+/* ---- quantization ---------------------------------------------------------
+ * qlora_nf4_quantize — blockwise NF4 quantization with double quantization
+ * (ozercemkelahmet.com "QLoRA", How it works, Steps 1-3 and "A worked
+ * example"; ai360xpert.com "QLoRA", How It Works item 2).
+ *
+ *   w          device, bf16 [numel]            input weights (flat row-major)
+ *   numel      > 0
+ *   codes      device, uint8 [ceil(numel/2)]    output, see "The NF4 store"
+ *   absmax_q   device, uint8 [ceil(numel/64)]   output
+ *   absmax_s2  device, float [num_groups]       output
+ * Per block of 64: c = max|w|; each value maps to the index of the nearest
+ * level of fl32(w / c) (ties to the lower index; c = 0 gives index 7, the
+ * level 0). Per group of 256 constants: s2 = max c and
+ * absmax_q = round_half_even(255 * fl32(c / s2)) (0 when s2 = 0).
+ * A short final block or group takes its maximum over the values present.
+ * Errors: INVALID_ARG for a null pointer or numel <= 0; UNSUPPORTED if `w`
+ * is not 2-byte aligned. Needs no workspace. */
+int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
+                       uint8_t* absmax_q, float* absmax_s2, void* stream);
+
+/* qlora_nf4_dequantize — expand a store to float32 w' (the formula in
+ * "The NF4 store"; ozercemkelahmet.com "QLoRA", "A worked example" step 4).
+ *   out        device, float [numel]
+ * Errors: INVALID_ARG for a null pointer or numel <= 0; UNSUPPORTED if
+ * `out` is not 4-byte aligned. */
+int qlora_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
+                         const float* absmax_s2, int64_t numel, float* out,
+                         void* stream);
+
+/* qlora_nf4_dequantize_bf16 — as above, but writes the bf16 compute weight
+ * bf16(w') (ozercemkelahmet.com "QLoRA", Step 5: the block is dequantized
+ * into the compute type). `out` is device uint16 [numel]. */
+int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
+                              const float* absmax_s2, int64_t numel,
+                              uint16_t* out, void* stream);
+
+/* ---- the linear layer ------------------------------------------------------
+ * Shapes: X [M x K], frozen weight W [N x K] in the NF4 store (numel = N*K,
+ * blocks run along K), A [K x r], B [r x N], Y and dY [M x N].
+ * scale = alpha / r is computed by the caller.
+ *
+ * Workspace: `ws` is device memory of at least
+ *   qlora_linear_workspace_bytes(M, N, K, r)
+ * bytes, 256-byte aligned, owned by the caller; it may be reused between
+ * calls that do not overlap. Its contents on entry do not matter. */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* qlora_linear_fwd — Y = X bf16(W')^T + scale * (X A) B
+ * (ozercemkelahmet.com "QLoRA", Step 5, written there in column form
+ * y = dequant(W) x + (alpha/r) B(Ax); crackai.dev "QLoRA: Efficient
+ * Finetuning of Quantized LLMs", Training Flow: dequantize to bf16 on the fly
+ * and compute with LoRA).
+ *   X        device bf16 [M x K]
+ *   codes, absmax_q, absmax_s2   the NF4 store of W, numel = N*K
+ *   A        device bf16 [K x r];  B  device bf16 [r x N]
+ *   Y        device bf16 [M x N]   output (bf16 of the float32 accumulation)
+ *   T_out    device float [M x r]  optional output: T = X A (for the
+ *                                  backward); NULL to skip
+ * Products of bf16 values accumulate in float32. M <= 16 takes a
+ * memory-bound split-K GEMV path; larger M takes an MFMA GEMM path.
+ * Errors: INVALID_ARG (null X/codes/absmax/A/B/Y, non-positive M, N, K);
+ * UNSUPPORTED (K % 64 != 0, r outside [1, 256], X/A/B/Y not 16-byte
+ * aligned); WORKSPACE (ws NULL or too small). */
+int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes,
+                     const uint8_t* absmax_q, const float* absmax_s2,
+                     const uint16_t* A, const uint16_t* B, int64_t M,
+                     int64_t N, int64_t K, int32_t r, float scale,
+                     uint16_t* Y, float* T_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* qlora_linear_bwd — gradients through the dequantized frozen weight into
+ * the input and the adapter; no gradient for the 4-bit weight
+ * (ozercemkelahmet.com "QLoRA", Step 6; crackai.dev "QLoRA: Efficient
+ * Finetuning of Quantized LLMs", Training Flow; ai360xpert.com "QLoRA",
+ * The Idea):
+ *   G  = dY B^T                   [M x r]
+ *   dX = dY bf16(W') + scale G A^T
+ *   dA = scale X^T G              [K x r]
+ *   dB = scale T^T dY             [r x N],  T = X A
+ *   dY       device bf16 [M x N]
+ *   X        device bf16 [M x K]
+ *   T        device float [M x r] from qlora_linear_fwd, or NULL to recompute
+ *   dX       device bf16 [M x K] output, or NULL to skip the input gradient
+ *   dA       device float [K x r] output (overwritten, not accumulated)
+ *   dB       device float [r x N] output (overwritten, not accumulated)
+ * Errors: as qlora_linear_fwd; dA and dB must not be NULL. */
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
+                     const uint8_t* codes, const uint8_t* absmax_q,
+                     const float* absmax_s2, const uint16_t* A,
+                     const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                     int32_t r, float scale, uint16_t* dX, float* dA,
+                     float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- diagnostics ------------------------------------------------------------ */
+
+/* Static text for a status code. */
+const char* qlora_status_string(int status);
+/* hipError_t of the calling thread's last QLORA_ERR_HIP (0 if none). */
+int qlora_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */
