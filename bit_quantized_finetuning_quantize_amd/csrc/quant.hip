@@ -111,8 +111,11 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
     for (int i = 0; i < 4; ++i) {
       const float a = bf16_lo(vals[r][i]);
       const float b = bf16_hi(vals[r][i]);
-      const uint32_t qa = (c > 0.0f) ? nf4_index(a / c) : 7u;
-      const uint32_t qb = (c > 0.0f) ? nf4_index(b / c) : 7u;
+      uint32_t qa = (c > 0.0f) ? nf4_index(a / c) : 7u;
+      uint32_t qb = (c > 0.0f) ? nf4_index(b / c) : 7u;
+      // nibbles past the end of the tensor stay 0
+      if (e0 + 2 * i >= numel) qa = 0u;
+      if (e0 + 2 * i + 1 >= numel) qb = 0u;
       word |= (qa | (qb << 4)) << (8 * i);
     }
     const int64_t byte0 = e0 / 2;
