@@ -2,7 +2,7 @@
 
 The library is required: there is no fallback. Import fails loudly when the
 shared object is missing; build it with
-`python -m bit_quantized_finetuning_quantize_amd.build`.
+`python bit_quantized_finetuning_quantize_amd/build.py`.
 """
 
 import ctypes
@@ -32,6 +32,12 @@ SIGNATURES = {
                                   _c_f32, _vp, _vp, _vp, _c_size, _vp]),
     "qlora_linear_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
                                   _c_i32, _c_f32, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "qlora_linear_fwd_profiled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                           _c_i32, _c_f32, _vp, _vp, _vp, _c_size, _vp, _vp,
+                                           _vp]),
+    "qlora_linear_bwd_profiled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
+                                           _c_i64, _c_i32, _c_f32, _vp, _vp, _vp, _vp, _c_size,
+                                           _vp, _vp, _vp]),
     "qlora_status_string": (ctypes.c_char_p, [_c_int]),
     "qlora_last_hip_error": (_c_int, []),
 }
@@ -41,7 +47,7 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m bit_quantized_finetuning_quantize_amd.build` (hipcc, gfx950)")
+            "`python bit_quantized_finetuning_quantize_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

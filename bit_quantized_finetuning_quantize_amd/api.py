@@ -112,8 +112,11 @@ def workspace(M, N, K, r, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def qlora_linear_fwd(X, W, A, B, scale, want_T=True, Y=None, T=None, ws=None):
-    """Y = X bf16(W')^T + scale (X A) B; returns (Y, T) with T fp32 or None."""
+def qlora_linear_fwd(X, W, A, B, scale, want_T=True, Y=None, T=None, ws=None, events=None):
+    """Y = X bf16(W')^T + scale (X A) B; returns (Y, T) with T fp32 or None.
+
+    `events`: optional (begin, end) raw hipEvent_t handles recorded around
+    the dominant kernel (profiling)."""
     M, K = X.shape
     N = W.shape[0]
     r = A.shape[1]
@@ -123,14 +126,20 @@ def qlora_linear_fwd(X, W, A, B, scale, want_T=True, Y=None, T=None, ws=None):
     if want_T and T is None:
         T = torch.empty(M, r, dtype=torch.float32, device=X.device)
     ws = ws if ws is not None else workspace(M, N, K, r, X.device)
-    _check(LIB.qlora_linear_fwd(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q), _ptr(W.absmax_s2),
-                                _ptr(A), _ptr(B), M, N, K, r, float(scale), _ptr(Y),
-                                _ptr(T) if want_T else None, _ptr(ws), ws.numel(), _stream()))
+    ev = events if events is not None else (None, None)
+    _check(LIB.qlora_linear_fwd_profiled(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q),
+                                         _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r,
+                                         float(scale), _ptr(Y), _ptr(T) if want_T else None,
+                                         _ptr(ws), ws.numel(), _stream(), ev[0], ev[1]))
     return Y, (T if want_T else None)
 
 
-def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, dB=None, ws=None):
-    """Returns (dX or None, dA fp32 [K x r], dB fp32 [r x N])."""
+def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, dB=None, ws=None,
+                     events=None):
+    """Returns (dX or None, dA fp32 [K x r], dB fp32 [r x N]).
+
+    `events`: optional (begin, end) raw hipEvent_t handles recorded around
+    the input-gradient kernel (profiling)."""
     M, N = dY.shape
     K = X.shape[1]
     r = A.shape[1]
@@ -141,8 +150,10 @@ def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, d
     dA = dA if dA is not None else torch.empty(K, r, dtype=torch.float32, device=X.device)
     dB = dB if dB is not None else torch.empty(r, N, dtype=torch.float32, device=X.device)
     ws = ws if ws is not None else workspace(M, N, K, r, X.device)
-    _check(LIB.qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(T), _ptr(W.codes), _ptr(W.absmax_q),
-                                _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r, float(scale),
-                                _ptr(dX) if want_dX else None, _ptr(dA), _ptr(dB), _ptr(ws),
-                                ws.numel(), _stream()))
+    ev = events if events is not None else (None, None)
+    _check(LIB.qlora_linear_bwd_profiled(_ptr(dY), _ptr(X), _ptr(T), _ptr(W.codes),
+                                         _ptr(W.absmax_q), _ptr(W.absmax_s2), _ptr(A), _ptr(B),
+                                         M, N, K, r, float(scale), _ptr(dX) if want_dX else None,
+                                         _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(),
+                                         ev[0], ev[1]))
     return (dX if want_dX else None), dA, dB

@@ -1,6 +1,7 @@
 """Build the HIP library (libqlora.so) for gfx950 with hipcc.
 
-Run as `python -m bit_quantized_finetuning_quantize_amd.build` or call
+Run as `python bit_quantized_finetuning_quantize_amd/build.py` (by path, so
+that the package, which loads the library, is not imported first) or call
 `build()`. The library is written next to this file, in-tree.
 """
 

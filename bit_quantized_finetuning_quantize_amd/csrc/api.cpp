@@ -89,10 +89,11 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) 
   return qlora::linear_workspace_bytes(M, N, K, r);
 }
 
-int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
-                     const float* absmax_s2, const uint16_t* A, const uint16_t* B, int64_t M,
-                     int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y, float* T_out,
-                     void* ws, size_t ws_bytes, void* stream) {
+int qlora_linear_fwd_profiled(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                              const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                              uint16_t* Y, float* T_out, void* ws, size_t ws_bytes, void* stream,
+                              void* ev_begin, void* ev_end) {
   if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
   int st = check_store(codes, absmax_q, absmax_s2);
   if (st != QLORA_OK) return st;
@@ -106,16 +107,28 @@ int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes, const uint8_t* abs
   if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
   qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev_begin);
+  hipEvent_t e1 = reinterpret_cast<hipEvent_t>(ev_end);
   if (M <= qlora::kGemvMaxM)
-    return hip_status(qlora::launch_fwd_gemv(X, W, A, B, (int)M, N, K, r, scale, Y, T_out, ws, s));
-  return hip_status(qlora::launch_fwd_gemm(X, W, A, B, M, N, K, r, scale, Y, T_out, ws, s));
+    return hip_status(
+        qlora::launch_fwd_gemv(X, W, A, B, (int)M, N, K, r, scale, Y, T_out, ws, s, e0, e1));
+  return hip_status(qlora::launch_fwd_gemm(X, W, A, B, M, N, K, r, scale, Y, T_out, ws, s, e0, e1));
 }
 
-int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, const uint8_t* codes,
-                     const uint8_t* absmax_q, const float* absmax_s2, const uint16_t* A,
-                     const uint16_t* B, int64_t M, int64_t N, int64_t K, int32_t r, float scale,
-                     uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
-                     void* stream) {
+int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                     const float* absmax_s2, const uint16_t* A, const uint16_t* B, int64_t M,
+                     int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y, float* T_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return qlora_linear_fwd_profiled(X, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, Y,
+                                   T_out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X, const float* T,
+                              const uint8_t* codes, const uint8_t* absmax_q,
+                              const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                              uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                              void* stream, void* ev_begin, void* ev_end) {
   if (!dY || !X || !A || !B || !dA || !dB) return QLORA_ERR_INVALID_ARG;
   int st = check_store(codes, absmax_q, absmax_s2);
   if (st != QLORA_OK) return st;
@@ -129,7 +142,18 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, cons
   if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
   qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
   return hip_status(qlora::launch_bwd(dY, X, T, W, A, B, M, N, K, r, scale, dX, dA, dB, ws,
-                                      reinterpret_cast<hipStream_t>(stream)));
+                                      reinterpret_cast<hipStream_t>(stream),
+                                      reinterpret_cast<hipEvent_t>(ev_begin),
+                                      reinterpret_cast<hipEvent_t>(ev_end)));
+}
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, const uint8_t* codes,
+                     const uint8_t* absmax_q, const float* absmax_s2, const uint16_t* A,
+                     const uint16_t* B, int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                     uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return qlora_linear_bwd_profiled(dY, X, T, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale,
+                                   dX, dA, dB, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 const char* qlora_status_string(int status) {

@@ -160,7 +160,8 @@ hipError_t launch_compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int
 
 hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A, const uint16_t* B,
                            int M, int64_t N, int64_t K, int r, float scale, uint16_t* Y,
-                           float* T_out, void* ws_, hipStream_t stream) {
+                           float* T_out, void* ws_, hipStream_t stream, hipEvent_t ev0,
+                           hipEvent_t ev1) {
   char* ws = reinterpret_cast<char*>(ws_);
   hipError_t e = launch_compute_T(X, A, M, N, K, r, scale, T_out, ws_, stream);
   if (e != hipSuccess) return e;
@@ -170,9 +171,13 @@ hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A, co
   const int64_t kc = gemv_kchunk(N, K);
   const int splits = (int)((K + kc - 1) / kc);
   dim3 grid((unsigned)((N + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)splits);
+  e = record_if(ev0, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(nf4_gemv_kernel, grid, dim3(256), 0, stream, X, W.codes, W.absmax_q,
                      W.absmax_s2, sT, r64, B, M, N, K, r, kc, Y, part);
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = record_if(ev1, stream);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = (int64_t)M * N;
   unsigned blocks = (unsigned)std::min<int64_t>(4096, (total + 255) / 256);

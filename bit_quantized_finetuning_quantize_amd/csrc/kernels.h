@@ -34,19 +34,28 @@ int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int M, int64_t N, int64_t K, int r,
                            float scale, uint16_t* Y, float* T_out, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, hipEvent_t ev0 = nullptr,
+                           hipEvent_t ev1 = nullptr);
 
 // Large-M forward: T = X A, then Y = [X | s T] [W' | B^T]^T on MFMA tiles.
 hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int64_t M, int64_t N, int64_t K,
                            int r, float scale, uint16_t* Y, float* T_out, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, hipEvent_t ev0 = nullptr,
+                           hipEvent_t ev1 = nullptr);
 
 // Backward: G = dY B^T, dX = [dY | s G] [W' ; A^T], dA = s X^T G, dB = s T^T dY.
 hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
                       Nf4Weight W, const uint16_t* A, const uint16_t* B,
                       int64_t M, int64_t N, int64_t K, int r, float scale,
                       uint16_t* dX, float* dA, float* dB, void* ws,
-                      hipStream_t stream);
+                      hipStream_t stream, hipEvent_t ev0 = nullptr,
+                      hipEvent_t ev1 = nullptr);
+
+// Records `ev` on `stream` when it is not null (profiling hooks around the
+// dominant launch of a call).
+inline hipError_t record_if(hipEvent_t ev, hipStream_t stream) {
+  return ev ? hipEventRecord(ev, stream) : hipSuccess;
+}
 
 }  // namespace qlora

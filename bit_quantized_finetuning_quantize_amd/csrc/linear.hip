@@ -214,7 +214,7 @@ hipError_t compute_T(const uint16_t* X, const uint16_t* Apad, int64_t M, int64_t
 hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int64_t M, int64_t N, int64_t K, int r,
                            float scale, uint16_t* Y, float* T_out, void* ws_,
-                           hipStream_t stream) {
+                           hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
   uint16_t* apad = reinterpret_cast<uint16_t*>(ws + w.apad);
@@ -240,13 +240,15 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
   cfg.splits = 1;
   cfg.steps_per_split = cfg.S1 + cfg.S2;
   cfg.epi = EpiBf16{Y, N, M, N};
-  return run<256, 128, LA1, LB1, LA2, LB2, EpiBf16, false>(cfg, stream);
+  QLORA_TRY(record_if(ev0, stream));
+  QLORA_TRY((run<256, 128, LA1, LB1, LA2, LB2, EpiBf16, false>(cfg, stream)));
+  return record_if(ev1, stream);
 }
 
 hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4Weight W,
                       const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                       int r, float scale, uint16_t* dX, float* dA, float* dB, void* ws_,
-                      hipStream_t stream) {
+                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
   float* part = reinterpret_cast<float*>(ws + w.part);
@@ -296,7 +298,9 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
     cfg.splits = 1;
     cfg.steps_per_split = cfg.S1 + cfg.S2;
     cfg.epi = EpiBf16{dX, K, M, K};
+    QLORA_TRY(record_if(ev0, stream));
     QLORA_TRY((run<256, 128, LA1, LB1, LA2, LB2, EpiBf16, false>(cfg, stream)));
+    QLORA_TRY(record_if(ev1, stream));
   }
   // 4a. dA = X^T (s G): P = K, Q = r64, contraction over M
   {

@@ -183,6 +183,30 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
                      int32_t r, float scale, uint16_t* dX, float* dA,
                      float* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- profiling variants ------------------------------------------------------
+ * Identical to qlora_linear_fwd / qlora_linear_bwd, and in addition record
+ * the caller's hipEvent_t `ev_begin` and `ev_end` (created by the caller,
+ * either may be NULL) on `stream` immediately before and after the launch of
+ * the call's dominant kernel: the fused NF4 product kernel of the forward
+ * (the GEMV for M <= 16, the MFMA contraction otherwise) and the fused
+ * input-gradient contraction of the backward (no events when dX is NULL).
+ * For measuring that kernel's duration with hipEventElapsedTime. */
+int qlora_linear_fwd_profiled(const uint16_t* X, const uint8_t* codes,
+                              const uint8_t* absmax_q, const float* absmax_s2,
+                              const uint16_t* A, const uint16_t* B, int64_t M,
+                              int64_t N, int64_t K, int32_t r, float scale,
+                              uint16_t* Y, float* T_out, void* ws,
+                              size_t ws_bytes, void* stream, void* ev_begin,
+                              void* ev_end);
+int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X,
+                              const float* T, const uint8_t* codes,
+                              const uint8_t* absmax_q, const float* absmax_s2,
+                              const uint16_t* A, const uint16_t* B, int64_t M,
+                              int64_t N, int64_t K, int32_t r, float scale,
+                              uint16_t* dX, float* dA, float* dB, void* ws,
+                              size_t ws_bytes, void* stream, void* ev_begin,
+                              void* ev_end);
+
 /* ---- diagnostics ------------------------------------------------------------ */
 
 /* Static text for a status code. */
