@@ -5,20 +5,25 @@
 // A workgroup owns a PT x QT tile of C and walks the contraction in steps of
 // 64. Waves 0-3 are consumers: each holds a (PT/2) x (QT/2) accumulator and
 // issues v_mfma_f32_32x32x16_bf16 on operand tiles read from LDS. Waves 4-7
-// are producers: they fetch the next steps from global memory into
-// registers, convert them (NF4 dequantization, transposition, float ->
-// bfloat16) and write them into the other half of a double-buffered LDS
-// stage, so the VALU work of dequantization overlaps the matrix cores.
+// are producers: they move the operand tiles of the coming steps into a
+// three-stage LDS ring, either with direct global->LDS buffer loads (plain
+// bf16 rows: no register or VALU cost) or through registers when a tile has
+// to be converted (NF4 dequantization, transposition).
 //
-// Operand tiles in LDS are [rows][64] bfloat16 with the contraction index
-// contiguous and rows padded to 72 elements (144 bytes), so that the 32
-// lanes reading one 16-byte fragment column touch distinct banks.
+// LDS tile layout: [rows][64] bf16, 128 bytes per row, the sixteen-byte
+// chunk c of row r stored at chunk position c ^ ((r >> 1) & 7). The XOR
+// swizzle keeps the 32 rows read by one MFMA fragment load on distinct
+// banks, and it is what a direct load produces when lane L of an
+// instruction fetches logical chunk (L % 8) ^ swizzle(row).
 //
-// A contraction may have two segments: steps [0, S1) come from one pair of
-// loaders and steps [S1, S1 + S2) from a second pair. The forward pass uses
-// the second segment for the adapter term (s T) B, the input-gradient pass
-// for (s G) A^T, so the LoRA products are accumulated by the same MFMA
-// tiles as the frozen-weight product.
+// Producer schedule (first segment): while the consumers work on step it,
+// the producers issue the direct loads of step it+2, convert the registers
+// of step it+1 into LDS, issue the register loads of step it+3, and wait
+// until the direct loads of step it+1 have landed. Every prefetch load is
+// issued unconditionally (buffer loads past the end of a tensor return 0
+// and their results are never stored), so the vector-memory counter waits
+// are exact constants. A second segment (steps S1 .. S1+S2-1, the LoRA
+// columns) is produced one step ahead without prefetch.
 #pragma once
 
 #include "common.h"
@@ -27,91 +32,141 @@ namespace qlora {
 namespace gemm {
 
 constexpr int kStep = 64;                 // contraction elements per step
-constexpr int kLdsStride = 72;            // bf16 elements per LDS row
+constexpr int kRowBytes = 128;            // one LDS tile row
+constexpr int kStages = 3;
 constexpr int kThreads = 512;             // 4 consumer + 4 producer waves
 constexpr int kProducerThreads = 256;
 
-__device__ __forceinline__ u32x4 ld_global_16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// byte offset of logical 16-byte chunk c of tile row `row`
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return row * kRowBytes + ((c ^ swz(row)) << 4);
 }
-__device__ __forceinline__ void st_lds_16(uint16_t* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7ffffff0LL) bytes = 0x7ffffff0LL;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
-__device__ __forceinline__ void st_lds_8(uint16_t* p, u32x2 v) {
-  *reinterpret_cast<u32x2*>(p) = v;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the stage ring. Each wave first waits for its own
+// LDS stores (lgkmcnt); the direct-load data of a stage is covered by the
+// producers' explicit vector-memory waits before this barrier. The asm
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
-// Loaders. Each has   Regs   (what one producer thread holds for one step),
-//   load(step, regs)        global -> registers (guarded, zero fill),
-//   store(regs, tile, lv)   registers -> LDS tile [R][72].
-// `step` counts 64-wide contraction steps from the start of the segment.
+// Loaders. Interface:
+//   kDirect   direct-load instructions per producer wave per step
+//   kRegLoads vector-memory register loads per producer thread per step
+//   Regs      per-thread registers of one step
+//   setup(tile_origin, t)           once per workgroup
+//   direct(step, tile, t)           issue direct global->LDS loads
+//   load(step, regs, t)             global -> registers
+//   store(regs, tile, tables, t)    registers -> LDS
+// `step` counts 64-wide contraction steps from the start of the segment;
+// `tile` is the LDS byte address of the operand tile of one stage. Loads
+// for steps past the end are allowed and harmless.
 
-// Rows of a row-major bf16 matrix with the contraction index contiguous:
-// tile row i = source row row0 + i, columns c0 .. c0+63.
-template <int R>
-struct LoadBf16Rows {
-  static constexpr int kChunks = R * 8 / kProducerThreads;  // 16-byte chunks per thread
-  const uint16_t* base;
-  int64_t ld;        // elements between source rows
-  int64_t rows;      // valid source rows
-  int64_t cols;      // valid contraction length (multiple of 8)
-  int64_t row0;
-  __device__ __forceinline__ void set_origin(int64_t o) { row0 = o; }
-  struct Regs { u32x4 v[kChunks]; };
-  __device__ __forceinline__ void load(int step, Regs& r, int t) const {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int id = t + i * kProducerThreads;
-      const int row = id >> 3, ch = id & 7;
-      const int64_t gr = row0 + row;
-      const int64_t gc = (int64_t)step * kStep + ch * 8;
-      if (gr < rows && gc < cols)
-        r.v[i] = ld_global_16(base + gr * ld + gc);
-      else
-        r.v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(const Regs& r, uint16_t* tile, const float*, int t) const {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int id = t + i * kProducerThreads;
-      const int row = id >> 3, ch = id & 7;
-      st_lds_16(tile + row * kLdsStride + ch * 8, r.v[i]);
-    }
-  }
+struct Tables {
+  const float* lv;   // 16 NF4 levels
+  const float* l8;   // 256 values fl(k / 255)
 };
 
-// Transposed bf16 source: tile row i = source COLUMN col0 + i, contraction
-// index = source row. Each thread moves 4 source rows x 8 source columns.
+// Rows of a row-major bf16 matrix, contraction contiguous, moved by direct
+// loads. Rows at or past `rows` read as zero. The contraction length of the
+// segment must be a multiple of 64.
 template <int R>
-struct LoadBf16Cols {
-  static constexpr int kUnits = R * 2;                       // (4 x 8) units per tile
-  static constexpr int kPer = (kUnits + kProducerThreads - 1) / kProducerThreads;
+struct DirectRows {
+  static constexpr int kDirect = R / 32;  // 1 KiB (8 rows) per instruction
+  static constexpr int kRegLoads = 0;
   const uint16_t* base;
-  int64_t ld;        // elements between source rows
-  int64_t rows;      // valid source rows (contraction length)
-  int64_t cols;      // valid source columns (multiple of 8)
-  int64_t col0;
-  __device__ __forceinline__ void set_origin(int64_t o) { col0 = o; }
+  int64_t ld;    // elements between rows
+  int64_t rows;  // valid rows
+  const void* rb; int64_t rn;  // buffer range of this tile (set in setup)
+  int voff[kDirect];
+  struct Regs {};
+  __device__ __forceinline__ void setup(int64_t row0, int t) {
+    rb = base + row0 * ld;
+    rn = (rows - row0) * ld * 2;
+    const int pw = t >> 6, lane = t & 63;
+#pragma unroll
+    for (int i = 0; i < kDirect; ++i) {
+      const int row = (pw * kDirect + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      voff[i] = (int)(row * ld * 2) + c * 16;
+    }
+  }
+  __device__ __forceinline__ void direct(int step, uint32_t tile, int t) const {
+    const int pw = t >> 6;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rb, rn);
+#pragma unroll
+    for (int i = 0; i < kDirect; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_void*)(uintptr_t)(tile + (uint32_t)((pw * kDirect + i) * 1024)), 16,
+          voff[i], step * (kStep * 2), 0, 0);
+  }
+  __device__ __forceinline__ void load(int, Regs&, int) const {}
+  __device__ __forceinline__ void store(const Regs&, uint32_t, const Tables&, int) const {}
+};
+
+// Transposed bf16 source through registers: tile row i = source column
+// col0 + i, contraction = source row. Each unit is 4 source rows x 8 source
+// columns. Source rows at or past `rows` read as zero.
+template <int R>
+struct ColsBf16 {
+  static constexpr int kUnits = R * 2;
+  static constexpr int kPer = (kUnits + kProducerThreads - 1) / kProducerThreads;
+  static constexpr int kDirect = 0;
+  static constexpr int kRegLoads = 4 * kPer;
+  const uint16_t* base;
+  int64_t ld;    // elements between source rows
+  int64_t rows;  // valid source rows (contraction length)
+  int64_t cols;  // valid source columns
+  const void* rb; int64_t rn;
+  int voff[kPer];
   struct Regs { u32x4 v[kPer][4]; };
-  __device__ __forceinline__ void load(int step, Regs& r, int t) const {
+  __device__ __forceinline__ void setup(int64_t col0, int t) {
+    rb = base + col0;
+    rn = rows * ld * 2 - col0 * 2;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int id = t + u * kProducerThreads;
       const int rg = id % (R / 8), cg = id / (R / 8);
-      const int64_t gcol = col0 + rg * 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t grow = (int64_t)step * kStep + cg * 4 + e;
-        if (id < kUnits && grow < rows && gcol < cols)
-          r.v[u][e] = ld_global_16(base + grow * ld + gcol);
-        else
-          r.v[u][e] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const bool ok = id < kUnits && col0 + rg * 8 < cols;
+      voff[u] = ok ? (int)((cg * 4) * ld * 2 + rg * 16) : 0x7ffffff0;
     }
   }
-  __device__ __forceinline__ void store(const Regs& r, uint16_t* tile, const float*, int t) const {
+  __device__ __forceinline__ void direct(int, uint32_t, int) const {}
+  __device__ __forceinline__ void load(int step, Regs& r, int) const {
+    const int soff = (int)((int64_t)step * kStep * ld * 2);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rb, rn);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r.v[u][e] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[u] + (int)(e * ld * 2), soff, 0));
+  }
+  __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables&, int t) const {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int id = t + u * kProducerThreads;
@@ -119,119 +174,151 @@ struct LoadBf16Cols {
       const int rg = id % (R / 8), cg = id / (R / 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // element e of each of the 4 source rows
         const int w = e >> 1, sh = (e & 1) * 16;
         const uint32_t a0 = (r.v[u][0][w] >> sh) & 0xffffu;
         const uint32_t a1 = (r.v[u][1][w] >> sh) & 0xffffu;
         const uint32_t a2 = (r.v[u][2][w] >> sh) & 0xffffu;
         const uint32_t a3 = (r.v[u][3][w] >> sh) & 0xffffu;
-        st_lds_8(tile + (rg * 8 + e) * kLdsStride + cg * 4,
-                 u32x2{a0 | (a1 << 16), a2 | (a3 << 16)});
+        const uint32_t a = tile + (uint32_t)(tile_off(rg * 8 + e, cg >> 1) + (cg & 1) * 8);
+        *(lds_u32x2*)(uintptr_t)a = u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
       }
     }
   }
 };
 
-// NF4 weight rows (forward): tile row i = weight row n0 + i (output feature),
-// contraction = input feature k; one step is exactly one 64-value block of a
-// row. Two threads per row, 32 codes each.
+// Dequantize 8 codes of one 32-bit word with block scale cs:
+// bf16(fl32(L[q] * cs)), two roundings, never fused.
+__device__ __forceinline__ void dequant_word(uint32_t w, float cs, const float* lv, uint32_t* out4) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = lv[(w >> (8 * j)) & 15u] * cs;
+    const float hi = lv[(w >> (8 * j + 4)) & 15u] * cs;
+    out4[j] = pack_bf16x2(lo, hi);
+  }
+}
+
+// NF4 weight rows (forward): tile row i = weight row n0 + i (output
+// feature), contraction = input feature k; a step is one 64-block of each
+// row. Two producer threads per row, 32 codes each.
 template <int R>
-struct LoadNf4Rows {
+struct Nf4Rows {
   static_assert(R * 2 == kProducerThreads, "two producer threads per row");
+  static constexpr int kDirect = 0;
+  static constexpr int kRegLoads = 3;
   const uint8_t* codes;
   const uint8_t* absmax_q;
   const float* absmax_s2;
-  int64_t N, K, n0;
-  __device__ __forceinline__ void set_origin(int64_t o) { n0 = o; }
+  int64_t N, K;
+  int64_t n0_;
+  int vcode, vq;
+  int blk0;  // block index of this thread's row at step 0 (< 2^31 by API limits)
   struct Regs { u32x4 c; uint32_t q8; float s2; };
-  __device__ __forceinline__ void load(int step, Regs& r, int t) const {
+  __device__ __forceinline__ void setup(int64_t n0, int t) {
     const int row = t >> 1, half = t & 1;
-    const int64_t n = n0 + row;
-    if (n < N) {
-      const int64_t e = n * K + (int64_t)step * kStep + half * 32;
-      r.c = ld_global_16(codes + e / 2);
-      const int64_t b = e / kBlock;
-      r.q8 = absmax_q[b];
-      r.s2 = absmax_s2[b / kGroup];
-    } else {
-      r.c = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      r.q8 = 0;
-      r.s2 = 0.0f;
-    }
+    n0_ = n0;
+    vcode = (int)(row * (K / 2)) + half * 16;
+    vq = (int)(row * (K / kBlock));
+    blk0 = (int)((n0 + row) * (K / kBlock));
   }
-  __device__ __forceinline__ void store(const Regs& r, uint16_t* tile, const float* lv, int t) const {
+  __device__ __forceinline__ void direct(int, uint32_t, int) const {}
+  __device__ __forceinline__ void load(int step, Regs& r, int) const {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + n0_ * (K / 2), (N - n0_) * (K / 2));
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(absmax_q + n0_ * (K / kBlock), (N - n0_) * (K / kBlock));
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(absmax_s2, ((N * K / kBlock) + kGroup - 1) / kGroup * 4);
+    r.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vcode, step * 32, 0));
+    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step, 0);
+    const int g = (blk0 + step) >> 8;
+    r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, g * 4, 0, 0));
+  }
+  __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {
+#pragma clang fp contract(off)
     const int row = t >> 1, half = t & 1;
-    const float cs = block_scale(r.q8, r.s2);
-    uint16_t* dst = tile + row * kLdsStride + half * 32;
+    const float cs = tb.l8[r.q8] * r.s2;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t c = r.c[w];
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = lv[(c >> (8 * j)) & 15u] * cs;
-        const float hi = lv[(c >> (8 * j + 4)) & 15u] * cs;
-        o[j] = pack_bf16x2(lo, hi);
-      }
-      st_lds_16(dst + w * 8, o);
+      uint32_t o[4];
+      dequant_word(r.c[w], cs, tb.lv, o);
+      const uint32_t a = tile + (uint32_t)tile_off(row, half * 4 + w);
+      *(lds_u32x4*)(uintptr_t)a = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
 };
 
 // NF4 weight, transposed (input gradient): tile row i = input feature
-// k0 + i, contraction = output feature n. Each thread dequantizes 4 weight
-// rows x 8 consecutive k (one 32-bit code word per row).
+// k0 + i, contraction = output feature n. Producer wave w (= t / 64) owns
+// tile rows 32 w .. 32 w + 31; lane t % 64 owns weight row n = 64 step +
+// t % 64 and loads its 32 codes (one 16-byte packet, inside one 64-block)
+// with one 8-bit constant and one second-level constant. The values are
+// written as 2-byte stores: for each k the 64 lanes of a wave fill one whole
+// 128-byte LDS row, so the transposition costs no bank conflicts.
 template <int R>
-struct LoadNf4Cols {
-  static constexpr int kUnits = R * 2;  // (4 rows x 8 k) units per tile
-  static_assert(kUnits == kProducerThreads, "one unit per producer thread");
+struct Nf4Cols {
+  static_assert(R == 128, "four producer waves x 32 tile rows");
+  static constexpr int kDirect = 0;
+  static constexpr int kRegLoads = 3;
   const uint8_t* codes;
   const uint8_t* absmax_q;
   const float* absmax_s2;
-  int64_t N, K, k0;
-  __device__ __forceinline__ void set_origin(int64_t o) { k0 = o; }
-  struct Regs { uint32_t c[4]; uint32_t q8[4]; float s2[4]; };
-  __device__ __forceinline__ void load(int step, Regs& r, int t) const {
-    const int kc = t % (R / 8), rg = t / (R / 8);
-    const int64_t k = k0 + kc * 8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t n = (int64_t)step * kStep + rg * 4 + e;
-      if (n < N && k < K) {
-        const int64_t el = n * K + k;
-        r.c[e] = *reinterpret_cast<const uint32_t*>(codes + el / 2);
-        const int64_t b = el / kBlock;
-        r.q8[e] = absmax_q[b];
-        r.s2[e] = absmax_s2[b / kGroup];
-      } else {
-        r.c[e] = 0x77777777u;
-        r.q8[e] = 0;
-        r.s2[e] = 0.0f;
-      }
-    }
+  int64_t N, K;
+  int vcode, vq;
+  int blk0;  // block index of (row t % 64, this k range) at step 0
+  struct Regs { u32x4 c; uint32_t q8; float s2; };
+  __device__ __forceinline__ void setup(int64_t k0, int t) {
+    const int nl = t & 63, kq = t >> 6;
+    const int64_t k = k0 + kq * 32;
+    const bool ok = k < K;
+    const int64_t e = (int64_t)nl * K + k;
+    vcode = ok ? (int)(e / 2) : 0x7ffffff0;
+    vq = ok ? (int)(e / kBlock) : 0x7ffffff0;
+    blk0 = (int)(e / kBlock);
   }
-  __device__ __forceinline__ void store(const Regs& r, uint16_t* tile, const float* lv, int t) const {
-    const int kc = t % (R / 8), rg = t / (R / 8);
-    float cs[4];
+  __device__ __forceinline__ void direct(int, uint32_t, int) const {}
+  __device__ __forceinline__ void load(int step, Regs& r, int) const {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes, (N * K) / 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(absmax_q, (N * K) / kBlock);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(absmax_s2, ((N * K / kBlock) + kGroup - 1) / kGroup * 4);
+    const int kb = (int)(K / kBlock);
+    r.c = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vcode, step * kStep * (int)(K / 2), 0));
+    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step * kStep * kb, 0);
+    const int g = (blk0 + step * kStep * kb) >> 8;
+    r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, g * 4, 0, 0));
+  }
+  __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {
+#pragma clang fp contract(off)
+    const int nl = t & 63, kq = t >> 6;
+    const float cs = tb.l8[r.q8] * r.s2;
+    const uint32_t col = (uint32_t)((nl & 7) * 2);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cs[e] = block_scale(r.q8[e], r.s2[e]);
+    for (int w = 0; w < 4; ++w) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = lv[(r.c[e] >> (4 * j)) & 15u] * cs[e];
-      st_lds_8(tile + (kc * 8 + j) * kLdsStride + rg * 4,
-               u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+      for (int j = 0; j < 4; ++j) {
+        const float lo = tb.lv[(r.c[w] >> (8 * j)) & 15u] * cs;
+        const float hi = tb.lv[(r.c[w] >> (8 * j + 4)) & 15u] * cs;
+        const uint32_t pk = pack_bf16x2(lo, hi);
+        const int row = kq * 32 + w * 8 + 2 * j;  // k of the low half
+        const uint32_t a0 = tile + (uint32_t)tile_off(row, nl >> 3) + col;
+        const uint32_t a1 = tile + (uint32_t)tile_off(row + 1, nl >> 3) + col;
+        *(__attribute__((address_space(3))) uint16_t*)(uintptr_t)a0 = (uint16_t)(pk & 0xffffu);
+        *(__attribute__((address_space(3))) uint16_t*)(uintptr_t)a1 = (uint16_t)(pk >> 16);
+      }
     }
   }
 };
 
 // A segment that is never used.
 struct LoadNone {
+  static constexpr int kDirect = 0;
+  static constexpr int kRegLoads = 0;
   struct Regs {};
-  __device__ __forceinline__ void set_origin(int64_t) {}
+  __device__ __forceinline__ void setup(int64_t, int) {}
+  __device__ __forceinline__ void direct(int, uint32_t, int) const {}
   __device__ __forceinline__ void load(int, Regs&, int) const {}
-  __device__ __forceinline__ void store(const Regs&, uint16_t*, const float*, int) const {}
+  __device__ __forceinline__ void store(const Regs&, uint32_t, const Tables&, int) const {}
 };
 
 // ---------------------------------------------------------------------------
@@ -255,20 +342,24 @@ struct EpiPartial {
   }
 };
 
-}  // namespace gemm
-}  // namespace qlora
-
-namespace qlora {
-namespace gemm {
-
+// ---------------------------------------------------------------------------
 // Consumer: one 64-wide contraction step on the LDS tiles.
 template <int PT, int QT>
 struct Consumer {
   static constexpr int WP = PT / 2, WQ = QT / 2;   // wave tile
   static constexpr int BP = WP / 32, BQ = WQ / 32; // 32x32 MFMA blocks per wave
   floatx16 acc[BP][BQ];
+  int a_off[4], b_off[4];  // per-lane LDS byte offsets of sub-step kk, block 0
 
-  __device__ __forceinline__ void zero() {
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int wp = wave >> 1, wq = wave & 1;
+    const int r = lane & 31, half = lane >> 5;
+    // blocks of one wave are 32 rows apart, which leaves the swizzle unchanged
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      a_off[kk] = tile_off(wp * WP + r, 2 * kk + half);
+      b_off[kk] = tile_off(wq * WQ + r, 2 * kk + half);
+    }
 #pragma unroll
     for (int i = 0; i < BP; ++i)
 #pragma unroll
@@ -277,25 +368,42 @@ struct Consumer {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   }
 
-  __device__ __forceinline__ void step(const uint16_t* sA, const uint16_t* sB, int wave, int lane) {
-    const int wp = wave >> 1, wq = wave & 1;
-    const int r = lane & 31, half = lane >> 5;
+  __device__ __forceinline__ void frags(uint32_t sA, uint32_t sB, int kk, bf16x8 (&a)[BP],
+                                        bf16x8 (&b)[BQ]) const {
 #pragma unroll
-    for (int kk = 0; kk < kStep / 16; ++kk) {
-      const int coff = kk * 16 + half * 8;
-      bf16x8 a[BP], b[BQ];
+    for (int i = 0; i < BP; ++i)
+      a[i] = as_bf16x8(*(const lds_u32x4*)(uintptr_t)(sA + a_off[kk] + i * 32 * kRowBytes));
 #pragma unroll
-      for (int i = 0; i < BP; ++i)
-        a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(sA + (wp * WP + i * 32 + r) * kLdsStride + coff));
+    for (int j = 0; j < BQ; ++j)
+      b[j] = as_bf16x8(*(const lds_u32x4*)(uintptr_t)(sB + b_off[kk] + j * 32 * kRowBytes));
+  }
+  __device__ __forceinline__ void mma(const bf16x8 (&a)[BP], const bf16x8 (&b)[BQ]) {
+#pragma unroll
+    for (int i = 0; i < BP; ++i)
 #pragma unroll
       for (int j = 0; j < BQ; ++j)
-        b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(sB + (wq * WQ + j * 32 + r) * kLdsStride + coff));
-#pragma unroll
-      for (int i = 0; i < BP; ++i)
-#pragma unroll
-        for (int j = 0; j < BQ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  // four 16-deep sub-steps; the fragments of sub-step kk+1 are read while
+  // the matrix cores work on sub-step kk
+  __device__ __forceinline__ void step(uint32_t sA, uint32_t sB) {
+    bf16x8 a0[BP], b0[BQ], a1[BP], b1[BQ];
+    frags(sA, sB, 0, a0, b0);
+    frags(sA, sB, 1, a1, b1);
+    mma(a0, b0);
+    frags(sA, sB, 2, a0, b0);
+    mma(a1, b1);
+    frags(sA, sB, 3, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
+    // keep two sub-steps of fragment reads in flight ahead of the MFMAs
+    constexpr int kF = BP + BQ, kM = BP * BQ;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF, 0);  // LDS reads, kk = 0, 1
+    __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);      // MFMA kk = 0
+    __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk = 2
+    __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);      // MFMA kk = 1
+    __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk = 3
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kM, 0);  // MFMA kk = 2, 3
   }
 
   // Visit every accumulator element with its (p, q) tile coordinates.
@@ -315,7 +423,7 @@ struct Consumer {
   }
 };
 
-// The kernel body shared by every contraction.
+// Launch parameters of one contraction.
 //   grid.x = nP * nQ * splits, tile order: p fastest, then q, then split.
 //   Steps of the first segment: [0, S1); second segment: [S1, S1 + S2).
 //   A split covers a contiguous range of the combined steps.
@@ -325,52 +433,32 @@ struct Contraction {
   int nP, nQ, splits, S1, S2, steps_per_split;
 };
 
-// Producer side of one segment: steps [lo, hi) of the segment's own
-// numbering (local step = global step - seg0), with global iteration index
-// it0 for the first of them. Step `it` is stored into stage it&1 and is
-// followed by exactly one barrier. Loads run two steps ahead in two register
-// slots that are only named by compile-time constants.
-template <class LA, class LB>
-__device__ __forceinline__ void produce_segment(const LA& la, const LB& lb, int lo, int hi,
-                                                int it0, uint16_t* smem, int stage_elems,
-                                                int a_rows, const float* lv, int t) {
-  const int L = hi - lo;
-  if (L <= 0) return;
-  typename LA::Regs ra0, ra1;
-  typename LB::Regs rb0, rb1;
-  la.load(lo, ra0, t); lb.load(lo, rb0, t);
-  if (L > 1) { la.load(lo + 1, ra1, t); lb.load(lo + 1, rb1, t); }
-  for (int i = 0; i < L; i += 2) {
-    {
-      uint16_t* sA = smem + ((it0 + i) & 1) * stage_elems;
-      la.store(ra0, sA, lv, t);
-      lb.store(rb0, sA + a_rows * kLdsStride, lv, t);
-      if (i + 2 < L) { la.load(lo + i + 2, ra0, t); lb.load(lo + i + 2, rb0, t); }
-    }
-    __syncthreads();
-    if (i + 1 >= L) break;
-    {
-      uint16_t* sA = smem + ((it0 + i + 1) & 1) * stage_elems;
-      la.store(ra1, sA, lv, t);
-      lb.store(rb1, sA + a_rows * kLdsStride, lv, t);
-      if (i + 3 < L) { la.load(lo + i + 3, ra1, t); lb.load(lo + i + 3, rb1, t); }
-    }
-    __syncthreads();
-  }
+template <int PT, int QT>
+constexpr size_t lds_bytes() {
+  return (size_t)kStages * (PT + QT) * kRowBytes + 256 * 4 + 16 * 4;
 }
 
+// One 512-thread workgroup per compute unit (the LDS ring takes most of the
+// 160 KiB), i.e. two waves per SIMD: let the register allocator use that.
 template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  __shared__ float s_lv[16];
-  constexpr int kStageElems = (PT + QT) * kLdsStride;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kStageBytes = (PT + QT) * kRowBytes;
+  constexpr uint32_t kBOff = PT * kRowBytes;
+  float* s_l8 = reinterpret_cast<float*>(smem + kStages * kStageBytes);
+  float* s_lv = s_l8 + 256;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
 
   const int tid = threadIdx.x;
   // the role split is per wave: keep it in a scalar register so that each
   // role's barriers are reached only by that role's waves
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  if (tid < 256) {
+#pragma clang fp contract(off)
+    s_l8[tid] = static_cast<float>(tid) / 255.0f;  // IEEE division
+  }
   if (tid < 16) s_lv[tid] = kNF4[tid];
 
   int id = blockIdx.x;
@@ -382,42 +470,97 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   const int s_end = min(total, s_begin + cfg.steps_per_split);
   const int n = max(0, s_end - s_begin);
 
-  __syncthreads();  // level table visible to every wave
+  __syncthreads();  // tables visible to every wave
+
+  auto stage = [&](int it) { return lds0 + (uint32_t)((it % kStages) * kStageBytes); };
 
   if (wave < 4) {
     // consumers: n steps, one barrier before each
     Consumer<PT, QT> cons;
-    cons.zero();
+    cons.init(wave, lane);
     for (int it = 0; it < n; ++it) {
-      __syncthreads();  // stage it&1 written
-      const uint16_t* sA = smem + (it & 1) * kStageElems;
-      cons.step(sA, sA + PT * kLdsStride, wave, lane);
+      stage_barrier();  // stage it % 3 written
+      const uint32_t sA = stage(it);
+      cons.step(sA, sA + kBOff);
     }
-    __syncthreads();  // matches the producers' final barrier
     const int64_t p0 = (int64_t)pt * PT, q0 = (int64_t)qt * QT;
     if constexpr (kPartial) {
       cons.for_each(wave, lane, [&](int p, int q, float v) { cfg.epi.put(p0 + p, q0 + q, v, split); });
     } else {
       cons.for_each(wave, lane, [&](int p, int q, float v) { cfg.epi.put(p0 + p, q0 + q, v); });
     }
-  } else {
-    // producers: store step it, then the barrier the consumers wait on
-    const int t = tid - kProducerThreads;
-    const int lo1 = s_begin, hi1 = min(s_end, cfg.S1);
-    const int lo2 = max(s_begin, cfg.S1), hi2 = s_end;
-    {
-      LA1 a = cfg.a1; LB1 b = cfg.b1;
-      a.set_origin((int64_t)pt * PT); b.set_origin((int64_t)qt * QT);
-      produce_segment(a, b, lo1, hi1, 0, smem, kStageElems, PT, s_lv, t);
-    }
-    {
-      LA2 a = cfg.a2; LB2 b = cfg.b2;
-      a.set_origin((int64_t)pt * PT); b.set_origin((int64_t)qt * QT);
-      produce_segment(a, b, lo2 - cfg.S1, hi2 - cfg.S1, max(0, hi1 - lo1), smem, kStageElems,
-                      PT, s_lv, t);
-    }
-    __syncthreads();  // final
+    return;
   }
+  if (n == 0) return;
+
+  // ---- producers: exactly n barriers, one after each produced step ----
+  const int t = tid - kProducerThreads;
+  const Tables tb{s_lv, s_l8};
+  // seg1 steps of this split: local [0, n1); seg2: local [n1, n)
+  const int n1 = max(0, min(s_end, cfg.S1) - s_begin);
+
+  LA2 a2 = cfg.a2; LB2 b2 = cfg.b2;
+  auto seg2_step = [&](int s) {  // local step s >= n1, loaded synchronously
+    typename LA2::Regs x; typename LB2::Regs y;
+    const int gs = s_begin + s - cfg.S1;
+    const uint32_t sa = stage(s);
+    a2.direct(gs, sa, t); b2.direct(gs, sa + kBOff, t);
+    a2.load(gs, x, t); b2.load(gs, y, t);
+    wait_vmcnt<0>();
+    a2.store(x, sa, tb, t); b2.store(y, sa + kBOff, tb, t);
+  };
+  if (n1 < n) { a2.setup((int64_t)pt * PT, t); b2.setup((int64_t)qt * QT, t); }
+
+  int it = 0;  // iteration it produces step it+1; step 0 comes from the prologue
+  if (n1 > 0) {
+    LA1 a1 = cfg.a1; LB1 b1 = cfg.b1;
+    a1.setup((int64_t)pt * PT, t);
+    b1.setup((int64_t)qt * QT, t);
+    constexpr int kReg = LA1::kRegLoads + LB1::kRegLoads;
+    constexpr int kDir = LA1::kDirect + LB1::kDirect;
+    typename LA1::Regs ra0, ra1;
+    typename LB1::Regs rb0, rb1;
+    const int g0 = s_begin;  // seg1 local step s is global step g0 + s
+
+    // prologue: step 0 complete in stage 0; direct loads of step 1; regs 1, 2
+    a1.direct(g0, stage(0), t); b1.direct(g0, stage(0) + kBOff, t);
+    a1.load(g0, ra0, t); b1.load(g0, rb0, t);
+    wait_vmcnt<0>();
+    a1.store(ra0, stage(0), tb, t); b1.store(rb0, stage(0) + kBOff, tb, t);
+    a1.direct(g0 + 1, stage(1), t); b1.direct(g0 + 1, stage(1) + kBOff, t);
+    a1.load(g0 + 1, ra1, t); b1.load(g0 + 1, rb1, t);
+    a1.load(g0 + 2, ra0, t); b1.load(g0 + 2, rb0, t);
+    stage_barrier();  // barrier #0: step 0 ready
+
+    // Iteration i (producing step i+1 < n1) with rA/rB holding step i+1.
+    auto iter = [&](int i, typename LA1::Regs& rA, typename LB1::Regs& rB) {
+      a1.direct(g0 + i + 2, stage(i + 2), t); b1.direct(g0 + i + 2, stage(i + 2) + kBOff, t);
+      a1.store(rA, stage(i + 1), tb, t); b1.store(rB, stage(i + 1) + kBOff, tb, t);
+      a1.load(g0 + i + 3, rA, t); b1.load(g0 + i + 3, rB, t);
+      wait_vmcnt<2 * kReg + kDir>();  // direct loads of step i+1 have landed
+    };
+    for (; it + 1 < n1 - 1; it += 2) {
+      iter(it, ra1, rb1);
+      stage_barrier();
+      iter(it + 1, ra0, rb0);
+      stage_barrier();
+    }
+    if (it < n1 - 1) {
+      iter(it, ra1, rb1);
+      stage_barrier();
+      ++it;
+    }
+    // it == n1 - 1 here
+  } else {
+    seg2_step(0);
+    stage_barrier();  // barrier #0
+  }
+  // tail: seg2 steps it+1 .. n-1, one per iteration
+  for (; it < n - 1; ++it) {
+    seg2_step(it + 1);
+    stage_barrier();
+  }
+  wait_vmcnt<0>();  // no direct load may outlive the workgroup's LDS
 }
 
 }  // namespace gemm

@@ -30,7 +30,7 @@ size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
 // Small-M forward (M <= kGemvMaxM): split-K GEMV with the LoRA epilogue.
 constexpr int kGemvMaxM = 16;
-int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K);
+int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int M, int64_t N, int64_t K, int r,
                            float scale, uint16_t* Y, float* T_out, void* ws,

@@ -49,7 +49,7 @@ int64_t choose_splits(int64_t tiles, int64_t steps) {
 // workspace carve-up (byte offsets, 256-aligned)
 struct WsLayout {
   int64_t r64, Mp;
-  size_t apad, t32, st, stt, g32, sg, sgt, part, total;
+  size_t apad, at, t32, st, stt, g32, sg, sgt, part, total;
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -59,6 +59,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
   w.apad = take((size_t)K * w.r64 * 2);
+  w.at = take((size_t)w.r64 * K * 2);
   w.t32 = take((size_t)M * r * 4);
   w.st = take((size_t)w.Mp * w.r64 * 2);
   w.stt = take((size_t)w.r64 * w.Mp * 2);
@@ -75,13 +76,33 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   consider(K, w.r64, choose_splits(ceil_div(K, 128) * (w.r64 / 64), ceil_div(M, 64)));
   consider(w.r64, N, choose_splits((w.r64 / 64) * ceil_div(N, 128), ceil_div(M, 64)));
   // the small-M forward path keeps its own partials here too
-  pe = std::max(pe, (size_t)gemv_partial_elems(M, N, K));
+  pe = std::max(pe, (size_t)gemv_partial_elems(M, N, K, r));
   w.part = take(pe * 4);
   w.total = off;
   return w;
 }
 
 }  // namespace
+
+// Every contraction used below, instantiated explicitly so that the host
+// side always emits its launch stub.
+namespace gemm {
+template __global__ void contraction_kernel<256, 128, DirectRows<256>, Nf4Rows<128>,
+    DirectRows<256>, ColsBf16<128>, EpiBf16, false>(
+    Contraction<256, 128, DirectRows<256>, Nf4Rows<128>, DirectRows<256>, ColsBf16<128>, EpiBf16>);
+template __global__ void contraction_kernel<256, 128, DirectRows<256>, Nf4Cols<128>,
+    DirectRows<256>, DirectRows<128>, EpiBf16, false>(
+    Contraction<256, 128, DirectRows<256>, Nf4Cols<128>, DirectRows<256>, DirectRows<128>, EpiBf16>);
+template __global__ void contraction_kernel<64, 64, DirectRows<64>, DirectRows<64>, LoadNone,
+    LoadNone, EpiPartial, true>(
+    Contraction<64, 64, DirectRows<64>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>);
+template __global__ void contraction_kernel<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone,
+    LoadNone, EpiPartial, true>(
+    Contraction<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>);
+template __global__ void contraction_kernel<64, 128, DirectRows<64>, ColsBf16<128>, LoadNone,
+    LoadNone, EpiPartial, true>(
+    Contraction<64, 128, DirectRows<64>, ColsBf16<128>, LoadNone, LoadNone, EpiPartial>);
+}  // namespace gemm
 
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
   return ws_layout(M, N, K, r).total;
@@ -92,16 +113,22 @@ namespace {
 // ---------------------------------------------------------------------------
 // small kernels
 
-// Apad[k][j] = A[k][j] for j < r, 0 for r <= j < r64.
-__global__ void pad_cols_kernel(const uint16_t* __restrict__ A, int64_t K, int r,
-                                int64_t r64, uint16_t* __restrict__ out) {
+// Apad[k][j] = A[k][j] for j < r, 0 for r <= j < r64; At = Apad^T [r64 x K].
+__global__ void adapter_prep_kernel(const uint16_t* __restrict__ A, int64_t K, int r,
+                                    int64_t r64, uint16_t* __restrict__ apad,
+                                    uint16_t* __restrict__ at) {
   const int64_t total = K * r64;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t k = i / r64, j = i % r64;
-    out[i] = (j < r) ? A[k * r + j] : (uint16_t)0;
+    const uint16_t v = (j < r) ? A[k * r + j] : (uint16_t)0;
+    apad[i] = v;
+    at[j * K + k] = v;
   }
 }
+
+hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, char* ws,
+                        hipStream_t stream);
 
 // Reduce split-K partials of an [M x r] low-rank product (partial layout
 // [split][M][ld]) and emit: float32 V (optional), bf16(s V) padded
@@ -151,7 +178,7 @@ unsigned grid_for(int64_t total, int threads = 256) {
 template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
 hipError_t run(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg, hipStream_t stream) {
   auto kern = contraction_kernel<PT, QT, LA1, LB1, LA2, LB2, Epi, kPartial>;
-  const size_t lds = (size_t)2 * (PT + QT) * kLdsStride * sizeof(uint16_t);
+  const size_t lds = lds_bytes<PT, QT>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -175,9 +202,9 @@ void set_steps(C& cfg, int64_t S1, int64_t S2, int64_t tiles) {
 template <class LB>
 hipError_t lowrank_partials(const uint16_t* a, int64_t lda, int64_t M, int64_t C, LB lb,
                             int64_t r64, float* part, int* splits_out, hipStream_t stream) {
-  using LA = LoadBf16Rows<64>;
+  using LA = DirectRows<64>;
   Contraction<64, 64, LA, LB, LoadNone, LoadNone, EpiPartial> cfg{};
-  cfg.a1 = LA{a, lda, M, C, 0};
+  cfg.a1 = LA{a, lda, M};
   cfg.b1 = lb;
   cfg.nP = (int)ceil_div(M, 64);
   cfg.nQ = (int)(r64 / 64);
@@ -193,14 +220,22 @@ hipError_t lowrank_partials(const uint16_t* a, int64_t lda, int64_t M, int64_t C
     if (e_ != hipSuccess) return e_;       \
   } while (0)
 
+hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, char* ws,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(adapter_prep_kernel, dim3(grid_for(K * w.r64)), dim3(256), 0, stream, A, K,
+                     r, w.r64, reinterpret_cast<uint16_t*>(ws + w.apad),
+                     reinterpret_cast<uint16_t*>(ws + w.at));
+  return hipGetLastError();
+}
+
 // T = X A -> out32 (optional), bf16(s T) [Mp x r64], bf16(s T)^T (optional).
-hipError_t compute_T(const uint16_t* X, const uint16_t* Apad, int64_t M, int64_t K, int r,
+hipError_t compute_T(const uint16_t* X, const uint16_t* At, int64_t M, int64_t K, int r,
                      const WsLayout& w, char* ws, float s, float* out32, bool transposed,
                      hipStream_t stream) {
   float* part = reinterpret_cast<float*>(ws + w.part);
   int splits = 0;
-  // Bop[j][k] = Apad[k][j]: transposed source, contraction over k
-  LoadBf16Cols<64> lb{Apad, w.r64, K, w.r64, 0};
+  // Bop[j][k] = A^T[j][k]: rows of the transposed, padded adapter
+  DirectRows<64> lb{At, K, w.r64};
   QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
   hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
                      part, splits, w.r64, M, r, w.r64, w.Mp, s, out32,
@@ -217,22 +252,20 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
-  uint16_t* apad = reinterpret_cast<uint16_t*>(ws + w.apad);
-  hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(K * w.r64)), dim3(256), 0, stream, A, K, r,
-                     w.r64, apad);
-  QLORA_TRY(hipGetLastError());
+  QLORA_TRY(prep_adapter(A, K, r, w, ws, stream));
+  const uint16_t* at = reinterpret_cast<const uint16_t*>(ws + w.at);
   float* t32 = T_out ? T_out : reinterpret_cast<float*>(ws + w.t32);
-  QLORA_TRY(compute_T(X, apad, M, K, r, w, ws, scale, t32, false, stream));
+  QLORA_TRY(compute_T(X, at, M, K, r, w, ws, scale, t32, false, stream));
 
-  using LA1 = LoadBf16Rows<256>;
-  using LB1 = LoadNf4Rows<128>;
-  using LA2 = LoadBf16Rows<256>;
-  using LB2 = LoadBf16Cols<128>;
+  using LA1 = DirectRows<256>;
+  using LB1 = Nf4Rows<128>;
+  using LA2 = DirectRows<256>;
+  using LB2 = ColsBf16<128>;
   Contraction<256, 128, LA1, LB1, LA2, LB2, EpiBf16> cfg{};
-  cfg.a1 = LA1{X, K, M, K, 0};
-  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K, 0};
-  cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.st), w.r64, M, w.r64, 0};
-  cfg.b2 = LB2{B, N, (int64_t)r, N, 0};  // Bop[n][j] = B[j][n]
+  cfg.a1 = LA1{X, K, M};
+  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K};
+  cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.st), w.r64, M};
+  cfg.b2 = LB2{B, N, (int64_t)r, N};  // Bop[n][j] = B[j][n]
   cfg.nP = (int)ceil_div(M, 256);
   cfg.nQ = (int)ceil_div(N, 128);
   cfg.S1 = (int)(K / 64);
@@ -252,15 +285,14 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
   float* part = reinterpret_cast<float*>(ws + w.part);
-  uint16_t* apad = reinterpret_cast<uint16_t*>(ws + w.apad);
-  hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(K * w.r64)), dim3(256), 0, stream, A, K, r,
-                     w.r64, apad);
-  QLORA_TRY(hipGetLastError());
+  QLORA_TRY(prep_adapter(A, K, r, w, ws, stream));
+  const uint16_t* apad = reinterpret_cast<const uint16_t*>(ws + w.apad);
+  const uint16_t* at = reinterpret_cast<const uint16_t*>(ws + w.at);
 
   // 1. G = dY B^T  (Bop[j][n] = B[j][n], rows j < r)
   {
     int splits = 0;
-    LoadBf16Rows<64> lb{B, N, (int64_t)r, N, 0};
+    DirectRows<64> lb{B, N, (int64_t)r};
     QLORA_TRY(lowrank_partials(dY, N, M, N, lb, w.r64, part, &splits, stream));
     hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
                        part, splits, w.r64, M, r, w.r64, w.Mp, scale,
@@ -277,20 +309,20 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
                        reinterpret_cast<uint16_t*>(ws + w.stt));
     QLORA_TRY(hipGetLastError());
   } else {
-    QLORA_TRY(compute_T(X, apad, M, K, r, w, ws, scale, reinterpret_cast<float*>(ws + w.t32),
+    QLORA_TRY(compute_T(X, at, M, K, r, w, ws, scale, reinterpret_cast<float*>(ws + w.t32),
                         true, stream));
   }
   // 3. dX = dY W' + (s G) A^T
   if (dX) {
-    using LA1 = LoadBf16Rows<256>;
-    using LB1 = LoadNf4Cols<128>;
-    using LA2 = LoadBf16Rows<256>;
-    using LB2 = LoadBf16Rows<128>;
+    using LA1 = DirectRows<256>;
+    using LB1 = Nf4Cols<128>;
+    using LA2 = DirectRows<256>;
+    using LB2 = DirectRows<128>;
     Contraction<256, 128, LA1, LB1, LA2, LB2, EpiBf16> cfg{};
-    cfg.a1 = LA1{dY, N, M, N, 0};
-    cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K, 0};
-    cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.sg), w.r64, M, w.r64, 0};
-    cfg.b2 = LB2{apad, w.r64, K, w.r64, 0};
+    cfg.a1 = LA1{dY, N, M};
+    cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K};
+    cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.sg), w.r64, M};
+    cfg.b2 = LB2{apad, w.r64, K};
     cfg.nP = (int)ceil_div(M, 256);
     cfg.nQ = (int)ceil_div(K, 128);
     cfg.S1 = (int)ceil_div(N, 64);
@@ -304,11 +336,11 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   }
   // 4a. dA = X^T (s G): P = K, Q = r64, contraction over M
   {
-    using LA = LoadBf16Cols<128>;   // Aop[k][m] = X[m][k]
-    using LB = LoadBf16Rows<64>;    // Bop[j][m] = (sG)^T[j][m]
+    using LA = ColsBf16<128>;    // Aop[k][m] = X[m][k]
+    using LB = DirectRows<64>;   // Bop[j][m] = (sG)^T[j][m]
     Contraction<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial> cfg{};
-    cfg.a1 = LA{X, K, M, K, 0};
-    cfg.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.sgt), w.Mp, w.r64, w.Mp, 0};
+    cfg.a1 = LA{X, K, M, K};
+    cfg.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.sgt), w.Mp, w.r64};
     cfg.nP = (int)ceil_div(K, 128);
     cfg.nQ = (int)(w.r64 / 64);
     set_steps(cfg, ceil_div(M, 64), 0, (int64_t)cfg.nP * cfg.nQ);
@@ -320,11 +352,11 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   }
   // 4b. dB = (s T)^T dY: P = r64, Q = N, contraction over M
   {
-    using LA = LoadBf16Rows<64>;    // Aop[j][m] = (sT)^T[j][m]
-    using LB = LoadBf16Cols<128>;   // Bop[n][m] = dY[m][n]
+    using LA = DirectRows<64>;   // Aop[j][m] = (sT)^T[j][m]
+    using LB = ColsBf16<128>;    // Bop[n][m] = dY[m][n]
     Contraction<64, 128, LA, LB, LoadNone, LoadNone, EpiPartial> cfg{};
-    cfg.a1 = LA{reinterpret_cast<const uint16_t*>(ws + w.stt), w.Mp, w.r64, w.Mp, 0};
-    cfg.b1 = LB{dY, N, M, N, 0};
+    cfg.a1 = LA{reinterpret_cast<const uint16_t*>(ws + w.stt), w.Mp, w.r64};
+    cfg.b1 = LB{dY, N, M, N};
     cfg.nP = (int)(w.r64 / 64);
     cfg.nQ = (int)ceil_div(N, 128);
     set_steps(cfg, ceil_div(M, 64), 0, (int64_t)cfg.nP * cfg.nQ);
@@ -339,19 +371,5 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
 
 // exported for the small-M path, which shares the workspace layout
 size_t ws_offset_part(int64_t M, int64_t N, int64_t K, int r) { return ws_layout(M, N, K, r).part; }
-size_t ws_offset_st(int64_t M, int64_t N, int64_t K, int r) { return ws_layout(M, N, K, r).st; }
-size_t ws_offset_apad(int64_t M, int64_t N, int64_t K, int r) { return ws_layout(M, N, K, r).apad; }
-size_t ws_offset_t32(int64_t M, int64_t N, int64_t K, int r) { return ws_layout(M, N, K, r).t32; }
-
-hipError_t launch_compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t N, int64_t K,
-                            int r, float scale, float* out32, void* ws_, hipStream_t stream) {
-  char* ws = reinterpret_cast<char*>(ws_);
-  const WsLayout w = ws_layout(M, N, K, r);
-  uint16_t* apad = reinterpret_cast<uint16_t*>(ws + w.apad);
-  hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(K * w.r64)), dim3(256), 0, stream, A, K, r,
-                     w.r64, apad);
-  QLORA_TRY(hipGetLastError());
-  return compute_T(X, apad, M, K, r, w, ws, scale, out32, false, stream);
-}
 
 }  // namespace qlora
