@@ -61,11 +61,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // float32 -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+// Two floats -> bf16x2 (RNE), lo in bits 0..15: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) {

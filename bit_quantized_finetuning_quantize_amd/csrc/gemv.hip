@@ -5,20 +5,21 @@
 //
 // Two launches per call.
 //
-// 1. nf4_gemv_main. The grid's x dimension holds two kinds of workgroups.
-//    GEMV workgroups (one per 64 weight rows and K split) stream the NF4
-//    store: a wave owns 16 rows; each lane issues, before any arithmetic,
-//    all of its 16-byte code packets (32 consecutive k of one row, inside
-//    one 64-block) and the few dword loads that hold their 8-bit and
-//    second-level constants, while the workgroup stages the split's token
-//    rows in LDS; then it dequantizes each packet in registers
-//    (level table and fl(q8/255) table in LDS) straight into the B operand
-//    of v_mfma_f32_16x16x32_bf16, with the tokens as the A operand (rows
-//    >= M are zero). The contraction index inside one MFMA is permuted
-//    identically for both operands, which leaves the sum unchanged.
-//    Adapter workgroups (one per 128-wide k chunk and 64 adapter columns)
-//    compute the chunk's partial of T = X A at the same time, staging A
-//    through LDS to transpose it into MFMA operands.
+// 1. nf4_gemv_main. The grid's x dimension holds two kinds of workgroups of
+//    kKQ x 4 waves. Adapter workgroups come first (one per kKQ x 128 k and
+//    64 adapter columns) and compute partials of T = X A, staging A through
+//    LDS to transpose it into MFMA operands. GEMV workgroups (one per 64
+//    weight rows and K split) stream the NF4 store: wave w owns 16 rows
+//    (w % 4) and one of kKQ k groups of the split (w / 4). Each lane issues,
+//    before any arithmetic, all of its 16-byte code packets (32 consecutive
+//    k of one row, inside one 64-block) and the few dword loads that hold
+//    their 8-bit and second-level constants, while the workgroup stages the
+//    split's token rows in LDS. It then dequantizes each packet in registers
+//    (level tables and the fl(q8/255) table in LDS) straight into the B
+//    operand of v_mfma_f32_16x16x32_bf16, with the tokens as the A operand
+//    (rows >= M are zero). The contraction index inside one MFMA is permuted
+//    identically for both operands, which leaves the sum unchanged. The k
+//    groups are summed through LDS in a fixed order.
 // 2. nf4_gemv_epilogue sums the float32 partials of Y and T in a fixed order
 //    (deterministic), adds s T B in float32 and rounds Y to bf16.
 #include "common.h"
@@ -30,9 +31,15 @@ namespace qlora {
 
 namespace {
 
-constexpr int kRowsPerBlock = 64;  // 4 waves x 16 rows
-constexpr int kChunk = 128;        // k per iteration per wave
-constexpr int kTCols = 64;         // adapter columns per adapter workgroup
+#ifndef QLORA_GEMV_KQ
+#define QLORA_GEMV_KQ 2
+#endif
+constexpr int kKQ = QLORA_GEMV_KQ;  // k groups per workgroup (4 waves each)
+constexpr int kThreads = 256 * kKQ;
+constexpr int kRowsPerBlock = 64;   // 4 row groups x 16 rows
+constexpr int kChunk = 128;         // k per packet column of a wave
+constexpr int kTK = kChunk * kKQ;   // k per adapter workgroup
+constexpr int kTCols = 64;          // adapter columns per adapter workgroup
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
   if (bytes > 0x7ffffff0LL) bytes = 0x7ffffff0LL;
@@ -40,16 +47,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int6
                                            0x00020000);
 }
 
-__device__ __forceinline__ bf16x8 dequant8(uint32_t word, float cs, const float* lv) {
+// 8 codes (one dword, element 2j in the low nibble of byte j) -> 8 bf16
+// weights bf16(fl(L[q] * cs)). Each byte of lo4 is 4 x its low nibble (a byte
+// offset into lv, 4-byte entries) and each byte of hi16 is 16 x its high
+// nibble (a byte offset into lv16, the levels at a 16-byte stride), so every
+// lookup address is one byte extract. The two masks are computed in asm so
+// that the compiler cannot fold them back into a shift and a mask per
+// element.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t word, float cs, const float* lv,
+                                           const float* lv16) {
 #pragma clang fp contract(off)
+  uint32_t lo4, hi16;
+  asm("v_lshlrev_b32 %0, 2, %1\n\tv_and_b32 %0, 0x3c3c3c3c, %0" : "=&v"(lo4) : "v"(word));
+  asm("v_and_b32 %0, 0xf0f0f0f0, %1" : "=v"(hi16) : "v"(word));
+  const char* b4 = reinterpret_cast<const char*>(lv);
+  const char* b16 = reinterpret_cast<const char*>(lv16);
   u32x4 o;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lo = lv[(word >> (8 * j)) & 15u] * cs;
-    const float hi = lv[(word >> (8 * j + 4)) & 15u] * cs;
+    const float lo = *reinterpret_cast<const float*>(b4 + ((lo4 >> (8 * j)) & 0xffu)) * cs;
+    const float hi = *reinterpret_cast<const float*>(b16 + ((hi16 >> (8 * j)) & 0xffu)) * cs;
     o[j] = pack_bf16x2(lo, hi);
   }
   return as_bf16x8(o);
+}
+
+// NF4 level q from immediates (a select chain), without a memory load.
+__device__ __forceinline__ float nf4_level(int q) {
+  float v = kNF4[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) v = (q == i) ? kNF4[i] : v;
+  return v;
 }
 
 struct GemvArgs {
@@ -60,132 +88,201 @@ struct GemvArgs {
   const uint16_t* A;
   int M, r;
   int64_t N, K;
-  int64_t kchunk;  // I * 128
   int ntiles;      // GEMV workgroups per split
   int splits;      // K splits of the GEMV workgroups
+  int tchunks;     // 512-wide k chunks of the adapter product
   int tblocks;     // 64-column groups of the adapter
   float* part_y;   // [splits][M][N]
-  float* part_t;   // [ceil(K/128)][M][r]
+  float* part_t;   // [tchunks][M][r]
 };
 
-// GEMV workgroup: weight rows [64 tile, 64 tile + 64), K split ks. The
-// token rows of the split (M x kchunk bf16) are staged once in LDS; each
-// lane then issues all of its code packets plus the few loads that cover
-// its block constants before any arithmetic.
+// LDS of one workgroup, reused by the three phases that need it.
 template <int I>
-__device__ void gemv_tile(const GemvArgs& a, int tile, int ks, const float* lv, const float* l8,
-                          uint16_t* sX) {
+struct alignas(16) Shared {
+  static constexpr int kX = 16 * I * kChunk;   // token rows [16][kc] bf16
+  static constexpr int kA = kTK * kTCols;      // adapter chunk [512][64] bf16
+  static constexpr int kU16 = kX > kA ? kX : kA;
+  float lv[16];
+  float lv16[64];    // level q at lv16[4 q] (16-byte stride)
+  float l8[256];
+  union {
+    uint16_t x[kU16];
+    floatx4 red[4 * kKQ][64];  // per-wave accumulators for the workgroup reduction
+  };
+};
+
+// GEMV workgroup: weight rows [64 tile, 64 tile + 64), K split ks of kc =
+// I*128. Wave w owns 16 rows (row group w & 3) and one of the kKQ k groups
+// of the split (w >> 2); the groups are summed in a fixed order through LDS.
+// The split's token rows are staged once in LDS; every global load is
+// issued before any arithmetic.
+template <int I>
+__device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
 #pragma clang fp contract(off)
-  constexpr int kOut = 0x7ffffff0;  // any offset past every range: loads return 0
+  constexpr int kOut = 0x7ffffff0;  // an offset past every range: the load returns 0
   constexpr int kc = I * kChunk;
+  constexpr int P = I / kKQ;        // packets per lane
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
-  const int64_t n = (int64_t)tile * kRowsPerBlock + wave * 16 + col;
+  const int rg = wave & 3, kq = wave >> 2;
+  const int64_t n = (int64_t)tile * kRowsPerBlock + rg * 16 + col;
   const int64_t kbeg = (int64_t)ks * kc;
   const int64_t kend = std::min<int64_t>(a.K, kbeg + kc);
-  const int m = col;
+  const int kw = kq * (kc / kKQ);   // this wave's first k inside the split
 
   const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.codes, a.N * a.K / 2);
   const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.absmax_q, a.N * a.K / kBlock);
-  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.absmax_s2, (a.N * a.K / kBlock + kGroup - 1) / kGroup * 4);
+  const __amdgpu_buffer_rsrc_t rs =
+      rsrc_of(a.absmax_s2, (a.N * a.K / kBlock + kGroup - 1) / kGroup * 4);
   const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.X, (int64_t)a.M * a.K * 2);
 
-  // codes: one 16-byte packet per iteration
-  u32x4 c[I];
+  // Every load is unconditional (an invalid one reads past the range and
+  // returns 0), so no wait covers a load that is not needed yet. The token
+  // rows go first: waiting for them then does not wait for the weights.
+  // A wave's units lie in one token row (kc / 8 >= 64): rows >= M are not
+  // loaded at all (a wave-uniform branch) and stored as zeros.
+  constexpr int kXU = 16 * kc / 8 / kThreads;  // 16-byte units per thread
+  static_assert(kc / 8 >= 64, "a wave's token units must lie in one row");
+  u32x4 xr[kXU];
+#pragma unroll
+  for (int j = 0; j < kXU; ++j) {
+    const int mm = (wave * 64 + kThreads * j) / (kc / 8);  // wave-uniform
+    xr[j] = u32x4{0u, 0u, 0u, 0u};
+    if (mm < a.M) {
+      const int k8 = ((tid + kThreads * j) % (kc / 8)) * 8;
+      const bool ok = kbeg + k8 < kend;
+      const uint32_t off = ((uint32_t)mm * (uint32_t)a.K + (uint32_t)(kbeg + k8)) * 2u;
+      xr[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (int)off : kOut, 0, 0));
+    }
+  }
+  // codes: packet p = 32 consecutive k of row n at kw + 128 p + 32 g
   const bool nok = n < a.N;
-  const int64_t e0 = n * a.K + kbeg + 32 * g;  // element of this lane's first packet
+  const int64_t e0 = n * a.K + kbeg + kw + 32 * g;
+  u32x4 c[P];
 #pragma unroll
-  for (int i = 0; i < I; ++i) {
-    const bool ok = nok && kbeg + i * kChunk + 32 * g < kend;
-    c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rc, ok ? (int)((e0 + i * kChunk) / 2) : kOut, 0, 0));
+  for (int p = 0; p < P; ++p) {
+    const bool ok = nok && kbeg + kw + p * kChunk + 32 * g < kend;
+    c[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rc, ok ? (int)((e0 + p * kChunk) / 2) : kOut, 0, 0));
   }
-  // 8-bit constants: packet i lies in block b0 + 2 i; one dword covers 4 blocks
+  // 8-bit constants: packet p lies in block b0 + 2 p; one dword holds 4 blocks
   const int64_t b0 = e0 / kBlock;
-  uint32_t qw[(2 * I + 3) / 4 + 1];
+  constexpr int kQW = (2 * P + 1) / 4 + 1;
+  uint32_t qw[kQW];
 #pragma unroll
-  for (int w = 0; w < (2 * I + 3) / 4 + 1; ++w) {
-    const int64_t bb = (b0 & ~3LL) + 4 * w;
-    qw[w] = nok ? __builtin_amdgcn_raw_buffer_load_b32(rq, (int)bb, 0, 0) : 0u;
-  }
-  // second-level constants: blocks b0 .. b0 + 2I - 2 span at most two groups
+  for (int w = 0; w < kQW; ++w)
+    qw[w] = __builtin_amdgcn_raw_buffer_load_b32(rq, nok ? (int)((b0 & ~3LL) + 4 * w) : kOut, 0, 0);
+  // second-level constants: blocks b0 .. b0 + 2P - 2 span at most two groups
   const int64_t g0 = b0 / kGroup;
   const float s2a = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)(g0 * 4) : kOut, 0, 0));
   const float s2b = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)((g0 + 1) * 4) : kOut, 0, 0));
-  // token rows of the split -> LDS [M][kc] (k >= kend is 0)
-  {
-    const int units = a.M * (kc / 8);  // 16-byte units
-    for (int u = tid; u < units; u += 256) {
-      const int mm = u / (kc / 8), k8 = (u % (kc / 8)) * 8;
-      const int64_t k = kbeg + k8;
-      const bool ok = k < kend;
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rx, ok ? (int)(((int64_t)mm * a.K + k) * 2) : kOut,
-                                                    0, 0));
-      *reinterpret_cast<u32x4*>(&sX[mm * kc + k8]) = v;
-    }
+  // lookup tables, built while the loads are in flight
+  if (tid < 16) {
+    sh.lv[tid] = nf4_level(tid);
+    sh.lv16[4 * tid] = nf4_level(tid);
+  }
+  if (tid < 256) {
+#pragma clang fp contract(off)
+    sh.l8[tid] = static_cast<float>(tid) / 255.0f;  // IEEE division
+  }
+  // all 16 rows are stored (rows >= M are zeros), so the reads need no branch
+#pragma unroll
+  for (int j = 0; j < kXU; ++j) {
+    const int u = tid + kThreads * j;
+    *reinterpret_cast<u32x4*>(&sh.x[(u / (kc / 8)) * kc + (u % (kc / 8)) * 8]) = xr[j];
   }
   __syncthreads();
 
   floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < I; ++i) {
-    const int64_t b = b0 + 2 * i;
+  for (int p = 0; p < P; ++p) {
+    const int64_t b = b0 + 2 * p;
     const int qi = (int)(b - (b0 & ~3LL));
     const uint32_t q8 = (qw[qi >> 2] >> (8 * (qi & 3))) & 0xffu;
     const float s2 = (b / kGroup == g0) ? s2a : s2b;
-    const float cs = l8[q8] * s2;
-    const int kl = i * kChunk + 32 * g;  // this lane's k inside the split
+    const float cs = sh.l8[q8] * s2;
+    const int kl = kw + p * kChunk + 32 * g;  // this lane's k inside the split
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x4 xv = {0u, 0u, 0u, 0u};  // token rows >= M are zero
-      if (m < a.M) xv = *reinterpret_cast<const u32x4*>(&sX[m * kc + kl + 8 * j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv), dequant8(c[i][j], cs, lv), acc,
-                                                    0, 0, 0);
+      // MFMA j takes elements 8j..8j+7 of every lane's packet, for the token
+      // operand and the weight operand alike: the sum over k is unchanged
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(&sh.x[col * kc + kl + 8 * j]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv), dequant8(c[p][j], cs, sh.lv,
+                                                                             sh.lv16),
+                                                    acc, 0, 0, 0);
     }
   }
-  // D[i][j]: lane holds rows i = 4 g + v (tokens), column j = col (weight row)
-  if (nok) {
+  __syncthreads();  // the token rows are dead: their LDS takes the reduction
+  sh.red[wave][lane] = acc;
+  __syncthreads();
+  if (kq == 0 && nok) {
+    floatx4 t = sh.red[rg][lane];
+#pragma unroll
+    for (int q = 1; q < kKQ; ++q) {
+      const floatx4 u = sh.red[rg + 4 * q][lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[v] += u[v];
+    }
+    // D[i][j]: this lane holds tokens i = 4 g + v of weight row j = col
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int mm = 4 * g + v;
-      if (mm < a.M) a.part_y[((int64_t)ks * a.M + mm) * a.N + n] = acc[v];
+      if (mm < a.M) a.part_y[((int64_t)ks * a.M + mm) * a.N + n] = t[v];
     }
   }
 }
 
-// A chunk (4 x 16 bytes per thread) and token fragments of one adapter chunk.
-struct AdapterChunk {
-  u32x4 a[4];   // 4 x 16 bytes of A (eight columns each)
-  u32x4 x[4];   // token fragments of the 4 MFMA steps
-};
-
-__device__ __forceinline__ void adapter_load(const GemvArgs& a, int64_t k0, int64_t kend, int j0,
-                                             AdapterChunk& c) {
+// Adapter workgroup: the partial of T = X A over one kTK-wide k chunk for
+// adapter columns [64 t, 64 t + 64). Wave w owns 16 columns (w & 3) of one
+// 128-wide part of the chunk (w >> 2); the parts are summed in a fixed
+// order. A is staged through LDS so that a lane can read 8 consecutive k of
+// one column.
+template <int I>
+__device__ void adapter_tile(const GemvArgs& a, int chunk, int t, Shared<I>& sh) {
   constexpr int kOut = 0x7ffffff0;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, g = (lane >> 4), m = lane & 15;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int cg = wave & 3, kq = wave >> 2;
+  const int64_t k0 = (int64_t)chunk * kTK;
+  const int64_t kend = std::min<int64_t>(a.K, k0 + kTK);
+  const int j0 = t * kTCols;
   const __amdgpu_buffer_rsrc_t ra = rsrc_of(a.A, a.K * a.r * 2);
   const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.X, (int64_t)a.M * a.K * 2);
+
+  // token fragments of this wave's 4 MFMA steps (row col, k 8 g of each 32)
+  u32x4 xf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t kb = k0 + kq * kChunk + s * 32 + 8 * g;
+    xf[s] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   rx, (col < a.M && kb < kend) ? (int)(((int64_t)col * a.K + kb) * 2) : kOut, 0,
+                   0));
+  }
+  // A chunk [512][64] -> LDS: thread loads 16-byte units (8 columns of a row)
+  constexpr int kAU = kTK * kTCols / 8 / kThreads;  // 4 16-byte units per thread
+  u32x4 av[kAU];
   if ((a.r & 7) == 0) {  // rows of A hold whole groups of eight columns
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + u * 256;  // 128 rows x 8 column groups
-      const int kk = e >> 3, j = j0 + (e & 7) * 8;
-      const int64_t k = k0 + kk;
+    for (int u = 0; u < kAU; ++u) {
+      const int e = tid + u * kThreads;
+      const int64_t k = k0 + (e >> 3);
+      const int j = j0 + (e & 7) * 8;
       const bool ok = k < kend && j < a.r;
-      c.a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             ra, ok ? (int)((k * a.r + j) * 2) : kOut, 0, 0));
+      av[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            ra, ok ? (int)((k * a.r + j) * 2) : kOut, 0, 0));
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + u * 256;
-      const int kk = e >> 3, j = j0 + (e & 7) * 8;
-      const int64_t k = k0 + kk;
+    for (int u = 0; u < kAU; ++u) {
+      const int e = tid + u * kThreads;
+      const int64_t k = k0 + (e >> 3);
+      const int j = j0 + (e & 7) * 8;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         uint32_t w = 0;
@@ -197,153 +294,221 @@ __device__ __forceinline__ void adapter_load(const GemvArgs& a, int64_t k0, int6
               ra, ok ? (int)((k * a.r + jj) * 2) : kOut, 0, 0);
           w |= (v & 0xffffu) << (16 * b);
         }
-        c.a[u][h] = w;
+        av[u][h] = w;
       }
     }
   }
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int64_t kb = k0 + s * 32 + 8 * g;
-    c.x[s] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                   rx, (m < a.M && kb < kend) ? (int)(((int64_t)m * a.K + kb) * 2) : kOut, 0, 0));
-  }
-}
-
-// Adapter workgroup: the partial of T over one 128-wide k chunk for
-// adapter columns [64 t, 64 t + 64); wave w owns 16 of them. The chunk of A
-// is staged through LDS so that each lane can read 8 consecutive k of one
-// column. One workgroup per chunk keeps every load of the adapter product in
-// flight at once.
-__device__ void adapter_tile(const GemvArgs& a, int chunk, int t, uint16_t* sA) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int64_t k0 = (int64_t)chunk * kChunk;
-  const int64_t kend = std::min<int64_t>(a.K, k0 + kChunk);
-  const int j0 = t * kTCols;
-  AdapterChunk cur;
-  adapter_load(a, k0, kend, j0, cur);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * 256;
-    *reinterpret_cast<u32x4*>(&sA[(e >> 3) * kTCols + (e & 7) * 8]) = cur.a[u];
+  for (int u = 0; u < kAU; ++u) {
+    const int e = tid + u * kThreads;
+    *reinterpret_cast<u32x4*>(&sh.x[(e >> 3) * kTCols + (e & 7) * 8]) = av[u];
   }
   __syncthreads();
   floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int s = 0; s < kChunk / 32; ++s) {
-    const int kl = s * 32 + 8 * g;  // this lane's 8 k inside the chunk
+  for (int s = 0; s < 4; ++s) {
+    const int kl = kq * kChunk + s * 32 + 8 * g;  // this lane's 8 k inside the chunk
     u32x4 wb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = sA[(kl + 2 * e) * kTCols + wave * 16 + col];
-      const uint32_t hi = sA[(kl + 2 * e + 1) * kTCols + wave * 16 + col];
+      const uint32_t lo = sh.x[(kl + 2 * e) * kTCols + cg * 16 + col];
+      const uint32_t hi = sh.x[(kl + 2 * e + 1) * kTCols + cg * 16 + col];
       wb[e] = lo | (hi << 16);
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.x[s]), as_bf16x8(wb), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xf[s]), as_bf16x8(wb), acc, 0, 0, 0);
   }
-  const int j = j0 + wave * 16 + col;
-  if (j < a.r) {
+  __syncthreads();
+  sh.red[wave][lane] = acc;
+  __syncthreads();
+  const int j = j0 + cg * 16 + col;
+  if (kq == 0 && j < a.r) {
+    floatx4 tt = sh.red[cg][lane];
+#pragma unroll
+    for (int q = 1; q < kKQ; ++q) {
+      const floatx4 u = sh.red[cg + 4 * q][lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tt[v] += u[v];
+    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int mm = 4 * g + v;
-      if (mm < a.M) a.part_t[((int64_t)chunk * a.M + mm) * a.r + j] = acc[v];
+      if (mm < a.M) a.part_t[((int64_t)chunk * a.M + mm) * a.r + j] = tt[v];
     }
   }
 }
 
+// Adapter workgroups come first in the grid so that they start first.
 template <int I>
-__global__ void __launch_bounds__(256) nf4_gemv_main(GemvArgs a) {
-  __shared__ float s_lv[16];
-  __shared__ float s_l8[256];
-  // adapter A chunk [128][64] or token rows [16][I * 128], never both
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[(kChunk * kTCols > 16 * I * kChunk)
-                                                           ? kChunk * kTCols
-                                                           : 16 * I * kChunk];
-  const int tid = threadIdx.x;
-  if (tid < 16) s_lv[tid] = kNF4[tid];
-  {
-#pragma clang fp contract(off)
-    s_l8[tid] = static_cast<float>(tid) / 255.0f;  // IEEE division
-  }
-  __syncthreads();
+__global__ void __launch_bounds__(kThreads) nf4_gemv_main(GemvArgs a) {
+  __shared__ Shared<I> sh;
   const int id = blockIdx.x;
-  const int ngemv = a.ntiles * a.splits;
-  if (id < ngemv) {
-    gemv_tile<I>(a, id % a.ntiles, id / a.ntiles, s_lv, s_l8, s_a);
-  } else {
-    const int u = id - ngemv;
-    adapter_tile(a, u / a.tblocks, u % a.tblocks, s_a);
-  }
+  const int nadapt = a.tchunks * a.tblocks;
+  if (id < nadapt)
+    adapter_tile<I>(a, id / a.tblocks, id % a.tblocks, sh);
+  else
+    gemv_tile<I>(a, (id - nadapt) % a.ntiles, (id - nadapt) / a.ntiles, sh);
 }
 
 // Y[m][n] = bf16( sum_s Py[s][m][n] + s * sum_j T[m][j] B[j][n] ),
-// T = sum_c Pt[c] (fixed order). Workgroup: 64 columns x all tokens. The
-// partial sums are loaded eight at a time so their latencies overlap.
+// T = sum_c Pt[c] (fixed orders). Workgroup: 64 columns x all tokens.
+// Thread: column n = n0 + tid % 64, tokens m = tid / 64 + 4 i. The first
+// pass of every input (Y partials of YS splits, BU 16-byte units of the B
+// tile, T partials of TS chunks for element tid) is issued before any of it
+// is used, branch-free, so the shapes the pass sizes cover take one round
+// trip; larger ones loop over further passes.
+template <int YS, int TS, int BU>
 __global__ void __launch_bounds__(256)
 nf4_gemv_epilogue(const float* __restrict__ part_y, const float* __restrict__ part_t,
                   int splits, int tsplits, int M, int64_t N, int r, const uint16_t* __restrict__ B,
                   float scale, uint16_t* __restrict__ Y, float* __restrict__ T_out) {
-  extern __shared__ float s_t[];  // [M][r]
+  constexpr int kOut = 0x7ffffff0;
+  extern __shared__ float s_dyn[];  // T [M][r] floats, then the B tile [r][64] bf16
+  float* s_t = s_dyn;
+  uint16_t* s_b = reinterpret_cast<uint16_t*>(s_dyn + M * r);
   const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t n = n0 + (tid & 63);
+  const bool nok = n < N;
+  const int mt = tid >> 6;
+  const __amdgpu_buffer_rsrc_t ry = rsrc_of(part_y, (int64_t)splits * M * N * 4);
+  const __amdgpu_buffer_rsrc_t rt = rsrc_of(part_t, (int64_t)tsplits * M * r * 4);
+  const __amdgpu_buffer_rsrc_t rb = rsrc_of(B, (int64_t)r * N * 2);
+  // offsets in 32 bits (each range is capped below 2^31 bytes), unsigned so
+  // that an unused one may wrap; an invalid load reads past the range
+  const uint32_t Nu = (uint32_t)N, Mu = (uint32_t)M, ru = (uint32_t)r;
+  const uint32_t nu = (uint32_t)n;
+  auto ld_y = [&](int s, int m) {
+    const bool ok = nok && m < M && s < splits;
+    const uint32_t off = (((uint32_t)s * Mu + (uint32_t)m) * Nu + nu) * 4u;
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(ry, ok ? (int)off : kOut, 0, 0));
+  };
+  auto ld_t = [&](int s, int e) {
+    const bool ok = e < M * r && s < tsplits;
+    const uint32_t off = ((uint32_t)s * Mu * ru + (uint32_t)e) * 4u;
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rt, ok ? (int)off : kOut, 0, 0));
+  };
+  auto ld_b = [&](int u) {  // unit u: row u / 8, columns n0 + 8 (u % 8) ..
+    const bool ok = u < 8 * r;
+    const uint32_t off = (((uint32_t)u >> 3) * Nu + (uint32_t)n0 + (uint32_t)(u & 7) * 8u) * 2u;
+    return __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? (int)off : kOut, 0, 0));
+  };
+  // first pass of everything
+  float py[4][YS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < YS; ++u) py[i][u] = ld_y(u, mt + 4 * i);
+  u32x4 bv[BU];
+#pragma unroll
+  for (int q = 0; q < BU; ++q) bv[q] = ld_b(tid + 256 * q);
+  float pt[TS];
+#pragma unroll
+  for (int u = 0; u < TS; ++u) pt[u] = ld_t(u, tid);
+  float tv = 0.0f;  // first pass of T for element tid
+#pragma unroll
+  for (int u = 0; u < TS; ++u) tv += pt[u];
+
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[i] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < YS; ++u) y[i] += py[i][u];
+  }
+  for (int s0 = YS; s0 < splits; s0 += YS) {  // more splits than one pass
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int u = 0; u < YS; ++u) py[i][u] = ld_y(s0 + u, mt + 4 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int u = 0; u < YS; ++u) y[i] += py[i][u];
+  }
+#pragma unroll
+  for (int q = 0; q < BU; ++q) {
+    const int u = tid + 256 * q;
+    if (u < 8 * r) *reinterpret_cast<u32x4*>(&s_b[u * 8]) = bv[q];
+  }
+  for (int u = tid + 256 * BU; u < 8 * r; u += 256)  // a B tile larger than one pass
+    *reinterpret_cast<u32x4*>(&s_b[u * 8]) = ld_b(u);
   for (int e = tid; e < M * r; e += 256) {
-    float v = 0.0f;
-    int s = 0;
-    for (; s + 8 <= tsplits; s += 8) {
-      float t[8];
+    float v = tv;
+    if (e != tid) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = part_t[(int64_t)(s + u) * M * r + e];
+      for (int u = 0; u < TS; ++u) pt[u] = ld_t(u, e);
+      v = 0.0f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v += t[u];
+      for (int u = 0; u < TS; ++u) v += pt[u];
     }
-    for (; s < tsplits; ++s) v += part_t[(int64_t)s * M * r + e];
+    for (int s0 = TS; s0 < tsplits; s0 += TS) {  // more chunks than one pass
+#pragma unroll
+      for (int u = 0; u < TS; ++u) pt[u] = ld_t(s0 + u, e);
+#pragma unroll
+      for (int u = 0; u < TS; ++u) v += pt[u];
+    }
     s_t[e] = v;
     if (T_out && blockIdx.x == 0) T_out[e] = v;
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 64 + (tid & 63);
-  if (n >= N) return;
-  for (int m = tid >> 6; m < M; m += 4) {
-    float y = 0.0f;
-    int s = 0;
-    for (; s + 8 <= splits; s += 8) {
-      float t[8];
+  if (!nok) return;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = part_y[((int64_t)(s + u) * M + m) * N + n];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) y += t[u];
+  for (int i = 0; i < 4; ++i) {
+    const int m = mt + 4 * i;
+    if (m < M) {
+      float l = 0.0f;
+      for (int j = 0; j < r; ++j) l += s_t[m * r + j] * bf16_to_f32(s_b[j * 64 + (tid & 63)]);
+      const float v = y[i] + scale * l;
+      Y[(int64_t)m * N + n] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
     }
-    for (; s < splits; ++s) y += part_y[((int64_t)s * M + m) * N + n];
-    float l = 0.0f;
-    int j = 0;
-    for (; j + 8 <= r; j += 8) {
-      float bv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) bv[u] = bf16_to_f32(B[(int64_t)(j + u) * N + n]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) l += s_t[m * r + j + u] * bv[u];
-    }
-    for (; j < r; ++j) l += s_t[m * r + j] * bf16_to_f32(B[(int64_t)j * N + n]);
-    y += scale * l;
-    Y[(int64_t)m * N + n] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
   }
 }
 
-// iterations per wave per split: fewer token rows leave room for deeper
-// prefetch
-int gemv_iters(int M) { return M <= 4 ? 8 : 4; }
+template <int YS, int TS>
+void launch_epilogue_bu(int bu, dim3 grid, size_t lds, hipStream_t stream, const float* part_y,
+                        const float* part_t, int splits, int tsplits, int M, int64_t N, int r,
+                        const uint16_t* B, float scale, uint16_t* Y, float* T_out) {
+  if (bu <= 1)
+    hipLaunchKernelGGL((nf4_gemv_epilogue<YS, TS, 1>), grid, dim3(256), lds, stream, part_y,
+                       part_t, splits, tsplits, M, N, r, B, scale, Y, T_out);
+  else if (bu <= 2)
+    hipLaunchKernelGGL((nf4_gemv_epilogue<YS, TS, 2>), grid, dim3(256), lds, stream, part_y,
+                       part_t, splits, tsplits, M, N, r, B, scale, Y, T_out);
+  else
+    hipLaunchKernelGGL((nf4_gemv_epilogue<YS, TS, 8>), grid, dim3(256), lds, stream, part_y,
+                       part_t, splits, tsplits, M, N, r, B, scale, Y, T_out);
+}
+
+// Pass sizes: the smallest of the instantiated ones that covers the shape.
+void launch_epilogue(dim3 grid, size_t lds, hipStream_t stream, const float* part_y,
+                     const float* part_t, int splits, int tsplits, int M, int64_t N, int r,
+                     const uint16_t* B, float scale, uint16_t* Y, float* T_out) {
+  const int bu = (8 * r + 255) / 256;
+  if (splits <= 4 && tsplits <= 16)
+    launch_epilogue_bu<4, 16>(bu, grid, lds, stream, part_y, part_t, splits, tsplits, M, N, r, B,
+                              scale, Y, T_out);
+  else
+    launch_epilogue_bu<8, 32>(bu, grid, lds, stream, part_y, part_t, splits, tsplits, M, N, r, B,
+                              scale, Y, T_out);
+}
+
+// k per GEMV workgroup: 8 packets columns of 128 (two per lane)
+constexpr int kIters = 8;
 
 }  // namespace
 
 int64_t gemv_splits(int64_t M, int64_t K) {
-  const int64_t kc = (int64_t)gemv_iters((int)M) * kChunk;
+  (void)M;
+  const int64_t kc = (int64_t)kIters * kChunk;
   return (K + kc - 1) / kc;
 }
 
 int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K, int r) {
   if (M > kGemvMaxM) return 0;
-  return gemv_splits(M, K) * M * N + (K + kChunk - 1) / kChunk * M * r;
+  return gemv_splits(M, K) * M * N + (K + kTK - 1) / kTK * M * r;
 }
 
 size_t ws_offset_part(int64_t M, int64_t N, int64_t K, int r);
@@ -353,28 +518,23 @@ hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A, co
                            float* T_out, void* ws_, hipStream_t stream, hipEvent_t ev0,
                            hipEvent_t ev1) {
   char* ws = reinterpret_cast<char*>(ws_);
-  const int I = gemv_iters(M);
   const int splits = (int)gemv_splits(M, K);
   float* part_y = reinterpret_cast<float*>(ws + ws_offset_part(M, N, K, r));
   float* part_t = part_y + (int64_t)splits * M * N;
-  const int tblocks = (r + kTCols - 1) / kTCols;
-  const int nchunks = (int)((K + kChunk - 1) / kChunk);
-  GemvArgs a{X, W.codes, W.absmax_q, W.absmax_s2, A, M, r, N, K, (int64_t)I * kChunk,
-             (int)((N + kRowsPerBlock - 1) / kRowsPerBlock), splits, tblocks, part_y, part_t};
-  dim3 grid((unsigned)(a.ntiles * splits + nchunks * tblocks));
+  GemvArgs a{X, W.codes, W.absmax_q, W.absmax_s2, A, M, r, N, K,
+             (int)((N + kRowsPerBlock - 1) / kRowsPerBlock), splits,
+             (int)((K + kTK - 1) / kTK), (r + kTCols - 1) / kTCols, part_y, part_t};
+  dim3 grid((unsigned)(a.ntiles * splits + a.tchunks * a.tblocks));
   hipError_t e = record_if(ev0, stream);
   if (e != hipSuccess) return e;
-  if (I == 8)
-    hipLaunchKernelGGL(nf4_gemv_main<8>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(nf4_gemv_main<4>, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(nf4_gemv_main<kIters>, grid, dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = record_if(ev1, stream);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)M * r * sizeof(float);
-  hipLaunchKernelGGL(nf4_gemv_epilogue, dim3((unsigned)((N + 63) / 64)), dim3(256), lds, stream,
-                     part_y, part_t, splits, nchunks, M, N, r, B, scale, Y, T_out);
+  const size_t lds = (size_t)M * r * sizeof(float) + (size_t)r * 64 * sizeof(uint16_t);
+  launch_epilogue(dim3((unsigned)((N + 63) / 64)), lds, stream, part_y, part_t, splits, a.tchunks,
+                  M, N, r, B, scale, Y, T_out);
   return hipGetLastError();
 }
 
