@@ -36,6 +36,129 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# HBM traffic of the forward contraction comes from two rocprofv3 --pmc runs
+# of `bench.py --pmc-pass` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
+# the same counter reads for a plain elementwise kernel of known size, and
+# is reported only while the kernel's sources are the ones it was taken on.
+PMC_FILE = os.path.join(ROOT, "profiles", "fwd_contraction_pmc.json")
+KERNEL_SOURCES = ["common.h", "gemm.h", "linear.hip"]
+CALIB_ELEMS = 64 << 20  # float32 in and out: 256 MiB read, 256 MiB written
+PMC_SHAPE = dict(M=2048, N=11008, K=4096, r=64, alpha=16)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_finetuning_quantize_amd", "csrc", f),
+                  "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_algorithmic_bytes(M, N, K, r, **_):
+    """Bytes the forward contraction must move once: X, the NF4 store, the
+    scaled adapter product s*T (bf16, rank padded to 64), B, and Y."""
+    r64 = (r + 63) // 64 * 64
+    nb = N * K // 64
+    return (2 * M * K + N * K // 2 + nb + (nb + 255) // 256 * 4 + 2 * M * r64 + 2 * r * N
+            + 2 * M * N)
+
+
+def pmc_pass():
+    """The dispatches the counter runs read: three calibration kernels, then
+    three forward passes of the gate projection (the contraction is one of
+    the launches of each)."""
+    import torch
+    import bit_quantized_finetuning_quantize_amd as q
+    import synthetic
+    dev = torch.device("cuda:0")
+    a = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 2.0, out=b)
+    torch.cuda.synchronize()
+    sh = PMC_SHAPE
+    W, X, A, B, _ = synthetic.linear_inputs(sh["M"], sh["N"], sh["K"], sh["r"], dev, seed=0,
+                                           base=synthetic.linear_base(0, 0))
+    st = q.qlora_nf4_quantize(W)
+    ws = q.workspace(sh["M"], sh["N"], sh["K"], sh["r"], dev)
+    for _ in range(3):
+        q.qlora_linear_fwd(X, st, A, B, sh["alpha"] / sh["r"], ws=ws)
+    torch.cuda.synchronize()
+    log("[pmc] done")
+
+
+def _pmc_values(d, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    calib, fwd = [], []
+    for fn in files:
+        with open(fn) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                v = float(row["Counter_Value"])
+                if "contraction_kernel" in name and "Nf4Rows" in name:
+                    fwd.append(v)
+                elif "MulFunctor" in name and row.get("Grid_Size") == str(CALIB_ELEMS // 4):
+                    calib.append(v)  # the calibration kernel: 4 floats per work-item
+    if len(calib) < 1 or len(fwd) < 1:
+        raise SystemExit(f"{counter}: calibration dispatches {len(calib)}, forward {len(fwd)}")
+    med = lambda x: sorted(x)[len(x) // 2]
+    return med(calib), med(fwd), len(calib), len(fwd)
+
+
+def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    cf, ff, ncf, nff = _pmc_values(fetch_dir, "FETCH_SIZE")
+    cw, fw, ncw, nfw = _pmc_values(write_dir, "WRITE_SIZE")
+    calib_bytes = 4 * CALIB_ELEMS
+    k_fetch = cf * 1024 / calib_bytes   # counter bytes per true byte
+    k_write = cw * 1024 / calib_bytes
+    fetch = ff * 1024 / k_fetch
+    write = fw * 1024 / k_write
+    alg = fwd_algorithmic_bytes(**PMC_SHAPE)
+    out = {
+        "kernel": "contraction_kernel (NF4 forward: DirectRows<256>, Nf4Rows<128> + LoRA segment)",
+        "workload": "gate projection W 11008x4096 NF4, X 2048x4096 bf16, r=64",
+        "source_hash": kernel_source_hash(),
+        "sources": KERNEL_SOURCES,
+        "calibration": {"kernel": "torch.mul(float32[64Mi], 2.0, out=float32[64Mi])",
+                        "bytes_read": calib_bytes, "bytes_written": calib_bytes,
+                        "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                        "fetch_factor": round(k_fetch, 4), "write_factor": round(k_write, 4),
+                        "dispatches": [ncf, ncw]},
+        "forward": {"FETCH_SIZE_KiB": ff, "WRITE_SIZE_KiB": fw, "dispatches": [nff, nfw],
+                    "fetch_bytes": round(fetch), "write_bytes": round(write),
+                    "traffic_bytes": round(fetch + write), "algorithmic_bytes": alg,
+                    "traffic_over_algorithmic": round((fetch + write) / alg, 3)},
+        "commands": [cmd_fetch, cmd_write],
+    }
+    os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
+    with open(PMC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def stored_traffic():
+    """(bytes per launch, detail) of the forward contraction, or (None, why)."""
+    try:
+        with open(PMC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if d.get("source_hash") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    f = d["forward"]
+    return f["traffic_bytes"], {"fetch_bytes": f["fetch_bytes"], "write_bytes": f["write_bytes"],
+                                "algorithmic_bytes": f["algorithmic_bytes"],
+                                "from": os.path.relpath(PMC_FILE, ROOT)}
+
+
 class HipEvents:
     """Raw hipEvent_t handles (libamdhip64) for timing single launches."""
 
@@ -154,7 +277,10 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     return res, projs
 
 
-def run_gemv(args, q, synthetic, torch, dev, ev):
+def run_gemv(args, q, synthetic, torch, dev):
+    """Decode GEMV per call, timed by replaying a HIP graph of `nstores`
+    back-to-back calls (each on a different weight store), so that host
+    launch overhead is not counted; a call is both of its launches."""
     N = K = 4096
     r, alpha = 16, 32
     s = alpha / r
@@ -168,36 +294,41 @@ def run_gemv(args, q, synthetic, torch, dev, ev):
     B = synthetic.normal((r, N), 0.01, dev, 0, synthetic.B_IDX)
     wbytes = stores[0].nbytes()
     out = {"weight_bytes_per_call": wbytes, "stores": nstores,
-           "rotating_bytes": wbytes * nstores}
+           "rotating_bytes": wbytes * nstores, "timing": "HIP graph replay of back-to-back calls"}
     for M in (1, 4, 16):
         X = synthetic.normal((M, K), 1.0, dev, 0, synthetic.X_IDX)
         Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        T = torch.empty(M, r, dtype=torch.float32, device=dev)
         ws = torch.empty(q.qlora_linear_workspace_bytes(M, N, K, r), dtype=torch.uint8,
                          device=dev)
-        for i in range(nstores):
-            q.qlora_linear_fwd(X, stores[i], A, B, s, Y=Y, T=T, ws=ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(nstores):
+                q.qlora_linear_fwd(X, stores[i], A, B, s, want_T=False, Y=Y, ws=ws)
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        calls = nstores * args.gemv_rounds
-        kev = [ev.pair() for _ in range(calls)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nstores):
+                q.qlora_linear_fwd(X, stores[i], A, B, s, want_T=False, Y=Y, ws=ws)
+        g.replay()
+        torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
-        for c in range(calls):
-            q.qlora_linear_fwd(X, stores[c % nstores], A, B, s, Y=Y, T=T, ws=ws, events=kev[c])
+        for _ in range(args.gemv_rounds):
+            g.replay()
         t1.record()
         torch.cuda.synchronize()
-        call_us = t0.elapsed_time(t1) * 1e3 / calls
-        kern_us = sum(ev.ms(p) for p in kev) * 1e3 / calls
-        gk = wbytes / (kern_us * 1e-6) / 1e9
-        out[f"M{M}"] = dict(call_us=call_us, kernel_us=kern_us,
-                            eff_weight_GBps_call=wbytes / (call_us * 1e-6) / 1e9,
-                            eff_weight_GBps_kernel=gk,
-                            roofline={"bound": "hbm", "achieved": round(gk, 1),
+        call_us = t0.elapsed_time(t1) * 1e3 / (args.gemv_rounds * nstores)
+        gbps = wbytes / (call_us * 1e-6) / 1e9
+        out[f"M{M}"] = dict(call_us=round(call_us, 3), eff_weight_GBps=round(gbps, 1),
+                            roofline={"bound": "hbm", "achieved": round(gbps, 1),
                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                      "frac": round(gk / PEAK_HBM_GBPS, 4)})
-        log(f"[gemv] M={M}: {call_us:.2f} us/call, kernel {kern_us:.2f} us, "
-            f"{out[f'M{M}']['eff_weight_GBps_kernel']:.0f} GB/s (kernel)")
+                                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                                      "per": "call (main + epilogue launch)"})
+        log(f"[gemv] M={M}: {call_us:.2f} us/call, {gbps:.0f} GB/s effective weight")
+        del g
     del stores
     return out
 
@@ -240,16 +371,27 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--gemv-stores", type=int, default=64)
-    ap.add_argument("--gemv-rounds", type=int, default=4)
+    ap.add_argument("--gemv-rounds", type=int, default=8)
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run only the dispatches the counter runs read")
+    ap.add_argument("--pmc-summarize", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "FETCH_CMD", "WRITE_CMD"),
+                    help="turn two rocprofv3 --pmc outputs into the stored traffic summary")
     args = ap.parse_args()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
-              "(the data-parallel exchange of dA/dB is described in DESIGN.md)",
+        print(f"bench.py: only one GPU is measured; --gpus {args.gpus} is not run",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_pass:
+        pmc_pass()
+        return
 
     import torch
     import bit_quantized_finetuning_quantize_amd as q
@@ -264,13 +406,14 @@ def main():
     gemv = None
     if not args.no_gemv:
         log("[bench] decode GEMV ...")
-        gemv = run_gemv(args, q, synthetic, torch, dev, ev)
+        gemv = run_gemv(args, q, synthetic, torch, dev)
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU oracle sample ...")
         cpu = cpu_baseline(args, projs, torch)
         log(f"[bench] cpu {cpu['value']:.4f} TFLOP/s")
     ev.close()
+    traffic, traffic_detail = stored_traffic()
 
     line = {
         "metric": METRIC,
@@ -299,7 +442,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre["fwd_kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_detail": traffic_detail,
             "flops_per_launch": pre["fwd_kernel_flops"],
             "avg_launch_ms": round(pre["fwd_kernel_ms"], 4),
         },

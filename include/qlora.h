@@ -64,7 +64,8 @@ extern "C" {
 enum {
   QLORA_OK = 0,
   QLORA_ERR_INVALID_ARG = -1, /* null required pointer, bad size, numel mismatch */
-  QLORA_ERR_UNSUPPORTED = -2, /* K % 64 != 0, r outside [1, 256], misaligned pointer */
+  QLORA_ERR_UNSUPPORTED = -2, /* K or N not a multiple of 64, r outside [1, 256],
+                                 a dimension above 2^30, misaligned pointer */
   QLORA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   QLORA_ERR_HIP = -4          /* a HIP launch failed; see qlora_last_hip_error() */
 };
@@ -106,7 +107,8 @@ void qlora_nf4_codebook(float* levels);
  * absmax_q = round_half_even(255 * fl32(c / s2)) (0 when s2 = 0).
  * A short final block or group takes its maximum over the values present.
  * Errors: INVALID_ARG for a null pointer or numel <= 0; UNSUPPORTED if `w`
- * is not 2-byte aligned. Needs no workspace. */
+ * is not 2-byte aligned or `codes` / `absmax_s2` not 4-byte aligned. Needs
+ * no workspace. */
 int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_s2, void* stream);
 
@@ -114,14 +116,15 @@ int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
  * "The NF4 store"; ozercemkelahmet.com "QLoRA", "A worked example" step 4).
  *   out        device, float [numel]
  * Errors: INVALID_ARG for a null pointer or numel <= 0; UNSUPPORTED if
- * `out` is not 4-byte aligned. */
+ * `codes` or `absmax_s2` is not 4-byte aligned or `out` not 16-byte
+ * aligned. */
 int qlora_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
                          const float* absmax_s2, int64_t numel, float* out,
                          void* stream);
 
 /* qlora_nf4_dequantize_bf16 — as above, but writes the bf16 compute weight
  * bf16(w') (ozercemkelahmet.com "QLoRA", Step 5: the block is dequantized
- * into the compute type). `out` is device uint16 [numel]. */
+ * into the compute type). `out` is device uint16 [numel], 16-byte aligned. */
 int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
                               const float* absmax_s2, int64_t numel,
                               uint16_t* out, void* stream);
@@ -149,10 +152,13 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  *   T_out    device float [M x r]  optional output: T = X A (for the
  *                                  backward); NULL to skip
  * Products of bf16 values accumulate in float32. M <= 16 takes a
- * memory-bound split-K GEMV path; larger M takes an MFMA GEMM path.
+ * memory-bound split-K GEMV path (two launches); larger M takes an MFMA
+ * GEMM path. Calls capture into a HIP graph (no memset, no allocation).
  * Errors: INVALID_ARG (null X/codes/absmax/A/B/Y, non-positive M, N, K);
- * UNSUPPORTED (K % 64 != 0, r outside [1, 256], X/A/B/Y not 16-byte
- * aligned); WORKSPACE (ws NULL or too small). */
+ * UNSUPPORTED (K or N not a multiple of 64, r outside [1, 256], M, N or K
+ * above 2^30; codes, X or B not 16-byte aligned, A or Y not 2-byte aligned,
+ * absmax_s2 or T_out not 4-byte aligned, ws not 256-byte aligned);
+ * WORKSPACE (ws NULL or ws_bytes below the query). */
 int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes,
                      const uint8_t* absmax_q, const float* absmax_s2,
                      const uint16_t* A, const uint16_t* B, int64_t M,
@@ -175,7 +181,8 @@ int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes,
  *   dX       device bf16 [M x K] output, or NULL to skip the input gradient
  *   dA       device float [K x r] output (overwritten, not accumulated)
  *   dB       device float [r x N] output (overwritten, not accumulated)
- * Errors: as qlora_linear_fwd; dA and dB must not be NULL. */
+ * Errors: as qlora_linear_fwd, with dY 16-byte aligned, dX 2-byte and
+ * T, dA, dB 4-byte aligned; dA and dB must not be NULL. */
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
                      const uint8_t* codes, const uint8_t* absmax_q,
                      const float* absmax_s2, const uint16_t* A,
