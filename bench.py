@@ -67,8 +67,8 @@ def fwd_algorithmic_bytes(M, N, K, r, **_):
 
 def pmc_pass():
     """The dispatches the counter runs read: three calibration kernels, then
-    three forward passes of the gate projection (the contraction is one of
-    the launches of each)."""
+    three forward and three backward passes of the gate projection (the
+    contractions are launches of each)."""
     import torch
     import bit_quantized_finetuning_quantize_amd as q
     import synthetic
@@ -83,8 +83,11 @@ def pmc_pass():
                                            base=synthetic.linear_base(0, 0))
     st = q.qlora_nf4_quantize(W)
     ws = q.workspace(sh["M"], sh["N"], sh["K"], sh["r"], dev)
+    dY = synthetic.normal((sh["M"], sh["N"]), 1e-3, dev, 0, synthetic.DY_IDX)
     for _ in range(3):
-        q.qlora_linear_fwd(X, st, A, B, sh["alpha"] / sh["r"], ws=ws)
+        Y, T = q.qlora_linear_fwd(X, st, A, B, sh["alpha"] / sh["r"], ws=ws)
+    for _ in range(3):
+        q.qlora_linear_bwd(dY, X, T, st, A, B, sh["alpha"] / sh["r"], ws=ws)
     torch.cuda.synchronize()
     log("[pmc] done")
 

@@ -87,8 +87,9 @@ __device__ __forceinline__ void stage_barrier() {
 // for steps past the end are allowed and harmless.
 
 struct Tables {
-  const float* lv;   // 16 NF4 levels
-  const float* l8;   // 256 values fl(k / 255)
+  const float* lv;    // 16 NF4 levels
+  const float* lv16;  // the same levels at a 16-byte stride
+  const float* l8;    // 256 values fl(k / 255)
 };
 
 // Rows of a row-major bf16 matrix, contraction contiguous, moved by direct
@@ -186,18 +187,6 @@ struct ColsBf16 {
   }
 };
 
-// Dequantize 8 codes of one 32-bit word with block scale cs:
-// bf16(fl32(L[q] * cs)), two roundings, never fused.
-__device__ __forceinline__ void dequant_word(uint32_t w, float cs, const float* lv, uint32_t* out4) {
-#pragma clang fp contract(off)
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lo = lv[(w >> (8 * j)) & 15u] * cs;
-    const float hi = lv[(w >> (8 * j + 4)) & 15u] * cs;
-    out4[j] = pack_bf16x2(lo, hi);
-  }
-}
-
 // NF4 weight rows (forward): tile row i = weight row n0 + i (output
 // feature), contraction = input feature k; a step is one 64-block of each
 // row. Two producer threads per row, 32 codes each.
@@ -235,14 +224,14 @@ struct Nf4Rows {
   }
   __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {
 #pragma clang fp contract(off)
+    // lookups by v_perm: the forward's consumers are bound by LDS
+    // bandwidth, so the producers keep their level lookups out of it
     const int row = t >> 1, half = t & 1;
-    const float cs = tb.l8[r.q8] * r.s2;
+    const PermTable pt = perm_table(tb.l8[r.q8] * r.s2);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t o[4];
-      dequant_word(r.c[w], cs, tb.lv, o);
       const uint32_t a = tile + (uint32_t)tile_off(row, half * 4 + w);
-      *(lds_u32x4*)(uintptr_t)a = u32x4{o[0], o[1], o[2], o[3]};
+      *(lds_u32x4*)(uintptr_t)a = dequant_word_perm(r.c[w], pt);
     }
   }
 };
@@ -290,16 +279,20 @@ struct Nf4Cols {
   }
   __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {
 #pragma clang fp contract(off)
+    // level lookups from LDS: this producer is bound by its 2-byte
+    // transposing stores, and the input-gradient consumers leave LDS
+    // bandwidth to spare
     const int nl = t & 63, kq = t >> 6;
-    const float cs = tb.l8[r.q8] * r.s2;
+    const float l8 = tb.l8[r.q8];
+    float lo[16], hi[16];
+    packet_levels(r.c, tb.lv, tb.lv16, lo, hi);
+    const float cs = l8 * r.s2;
     const uint32_t col = (uint32_t)((nl & 7) * 2);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float lo = tb.lv[(r.c[w] >> (8 * j)) & 15u] * cs;
-        const float hi = tb.lv[(r.c[w] >> (8 * j + 4)) & 15u] * cs;
-        const uint32_t pk = pack_bf16x2(lo, hi);
+        const uint32_t pk = pack_bf16x2(lo[4 * w + j] * cs, hi[4 * w + j] * cs);
         const int row = kq * 32 + w * 8 + 2 * j;  // k of the low half
         const uint32_t a0 = tile + (uint32_t)tile_off(row, nl >> 3) + col;
         const uint32_t a1 = tile + (uint32_t)tile_off(row + 1, nl >> 3) + col;
@@ -434,8 +427,8 @@ struct Contraction {
 };
 
 template <int PT, int QT>
-constexpr size_t lds_bytes() {
-  return (size_t)kStages * (PT + QT) * kRowBytes + 256 * 4 + 16 * 4;
+constexpr size_t lds_bytes() {  // dynamic LDS: the stage ring
+  return (size_t)kStages * (PT + QT) * kRowBytes;
 }
 
 // One 512-thread workgroup per compute unit (the LDS ring takes most of the
@@ -444,10 +437,13 @@ template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi,
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // lookup tables at fixed LDS addresses (the compiler folds them into the
+  // instruction offsets); the dynamic LDS holds the stage ring
+  __shared__ float s_lv[16];
+  __shared__ __attribute__((aligned(16))) float s_lv16[64];
+  __shared__ float s_l8[256];
   constexpr int kStageBytes = (PT + QT) * kRowBytes;
   constexpr uint32_t kBOff = PT * kRowBytes;
-  float* s_l8 = reinterpret_cast<float*>(smem + kStages * kStageBytes);
-  float* s_lv = s_l8 + 256;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
 
   const int tid = threadIdx.x;
@@ -459,7 +455,10 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
 #pragma clang fp contract(off)
     s_l8[tid] = static_cast<float>(tid) / 255.0f;  // IEEE division
   }
-  if (tid < 16) s_lv[tid] = kNF4[tid];
+  if (tid < 16) {
+    s_lv[tid] = nf4_level(tid);
+    s_lv16[4 * tid] = nf4_level(tid);
+  }
 
   int id = blockIdx.x;
   const int pt = id % cfg.nP; id /= cfg.nP;
@@ -473,13 +472,38 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   __syncthreads();  // tables visible to every wave
 
   auto stage = [&](int it) { return lds0 + (uint32_t)((it % kStages) * kStageBytes); };
+  // seg1 steps of this split: local [0, n1); seg2: local [n1, n)
+  const int n1 = max(0, min(s_end, cfg.S1) - s_begin);
+  const int g0 = s_begin;  // seg1 local step s is global step g0 + s
+  // An A operand of seg1 that only takes direct loads is moved by the
+  // consumer waves: the loads are vector-memory instructions that issue
+  // between their MFMAs, and the producers keep the register path.
+  constexpr bool kConsA = LA1::kDirect > 0 && LA1::kRegLoads == 0;
 
   if (wave < 4) {
     // consumers: n steps, one barrier before each
     Consumer<PT, QT> cons;
     cons.init(wave, lane);
+    LA1 a1 = cfg.a1;
+    if constexpr (kConsA) {
+      if (n1 > 0) {
+        a1.setup((int64_t)pt * PT, tid);
+        a1.direct(g0, stage(0), tid);
+        if (n1 > 1) a1.direct(g0 + 1, stage(1), tid);
+      }
+    }
     for (int it = 0; it < n; ++it) {
+      if constexpr (kConsA) {
+        // this wave's A loads of step it have landed (those of it+1 may fly)
+        if (it + 1 < n1) wait_vmcnt<LA1::kDirect>();
+        else if (it < n1) wait_vmcnt<0>();
+      }
       stage_barrier();  // stage it % 3 written
+      // stage (it+2) % 3 was last read in step it-1, which every consumer
+      // finished before this barrier
+      if constexpr (kConsA) {
+        if (it + 2 < n1) a1.direct(g0 + it + 2, stage(it + 2), tid);
+      }
       const uint32_t sA = stage(it);
       cons.step(sA, sA + kBOff);
     }
@@ -495,9 +519,7 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
 
   // ---- producers: exactly n barriers, one after each produced step ----
   const int t = tid - kProducerThreads;
-  const Tables tb{s_lv, s_l8};
-  // seg1 steps of this split: local [0, n1); seg2: local [n1, n)
-  const int n1 = max(0, min(s_end, cfg.S1) - s_begin);
+  const Tables tb{s_lv, s_lv16, s_l8};
 
   LA2 a2 = cfg.a2; LB2 b2 = cfg.b2;
   auto seg2_step = [&](int s) {  // local step s >= n1, loaded synchronously
@@ -514,27 +536,29 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   int it = 0;  // iteration it produces step it+1; step 0 comes from the prologue
   if (n1 > 0) {
     LA1 a1 = cfg.a1; LB1 b1 = cfg.b1;
-    a1.setup((int64_t)pt * PT, t);
+    if constexpr (!kConsA) a1.setup((int64_t)pt * PT, t);
     b1.setup((int64_t)qt * QT, t);
     constexpr int kReg = LA1::kRegLoads + LB1::kRegLoads;
-    constexpr int kDir = LA1::kDirect + LB1::kDirect;
+    constexpr int kDir = (kConsA ? 0 : LA1::kDirect) + LB1::kDirect;
     typename LA1::Regs ra0, ra1;
     typename LB1::Regs rb0, rb1;
-    const int g0 = s_begin;  // seg1 local step s is global step g0 + s
+    auto a1_direct = [&](int g, uint32_t sa) {
+      if constexpr (!kConsA) a1.direct(g, sa, t);
+    };
 
     // prologue: step 0 complete in stage 0; direct loads of step 1; regs 1, 2
-    a1.direct(g0, stage(0), t); b1.direct(g0, stage(0) + kBOff, t);
+    a1_direct(g0, stage(0)); b1.direct(g0, stage(0) + kBOff, t);
     a1.load(g0, ra0, t); b1.load(g0, rb0, t);
     wait_vmcnt<0>();
     a1.store(ra0, stage(0), tb, t); b1.store(rb0, stage(0) + kBOff, tb, t);
-    a1.direct(g0 + 1, stage(1), t); b1.direct(g0 + 1, stage(1) + kBOff, t);
+    a1_direct(g0 + 1, stage(1)); b1.direct(g0 + 1, stage(1) + kBOff, t);
     a1.load(g0 + 1, ra1, t); b1.load(g0 + 1, rb1, t);
     a1.load(g0 + 2, ra0, t); b1.load(g0 + 2, rb0, t);
     stage_barrier();  // barrier #0: step 0 ready
 
     // Iteration i (producing step i+1 < n1) with rA/rB holding step i+1.
     auto iter = [&](int i, typename LA1::Regs& rA, typename LB1::Regs& rB) {
-      a1.direct(g0 + i + 2, stage(i + 2), t); b1.direct(g0 + i + 2, stage(i + 2) + kBOff, t);
+      a1_direct(g0 + i + 2, stage(i + 2)); b1.direct(g0 + i + 2, stage(i + 2) + kBOff, t);
       a1.store(rA, stage(i + 1), tb, t); b1.store(rB, stage(i + 1) + kBOff, tb, t);
       a1.load(g0 + i + 3, rA, t); b1.load(g0 + i + 3, rB, t);
       wait_vmcnt<2 * kReg + kDir>();  // direct loads of step i+1 have landed

@@ -47,39 +47,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int6
                                            0x00020000);
 }
 
-// 8 codes (one dword, element 2j in the low nibble of byte j) -> 8 bf16
-// weights bf16(fl(L[q] * cs)). Each byte of lo4 is 4 x its low nibble (a byte
-// offset into lv, 4-byte entries) and each byte of hi16 is 16 x its high
-// nibble (a byte offset into lv16, the levels at a 16-byte stride), so every
-// lookup address is one byte extract. The two masks are computed in asm so
-// that the compiler cannot fold them back into a shift and a mask per
-// element.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t word, float cs, const float* lv,
-                                           const float* lv16) {
-#pragma clang fp contract(off)
-  uint32_t lo4, hi16;
-  asm("v_lshlrev_b32 %0, 2, %1\n\tv_and_b32 %0, 0x3c3c3c3c, %0" : "=&v"(lo4) : "v"(word));
-  asm("v_and_b32 %0, 0xf0f0f0f0, %1" : "=v"(hi16) : "v"(word));
-  const char* b4 = reinterpret_cast<const char*>(lv);
-  const char* b16 = reinterpret_cast<const char*>(lv16);
-  u32x4 o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lo = *reinterpret_cast<const float*>(b4 + ((lo4 >> (8 * j)) & 0xffu)) * cs;
-    const float hi = *reinterpret_cast<const float*>(b16 + ((hi16 >> (8 * j)) & 0xffu)) * cs;
-    o[j] = pack_bf16x2(lo, hi);
-  }
-  return as_bf16x8(o);
-}
-
-// NF4 level q from immediates (a select chain), without a memory load.
-__device__ __forceinline__ float nf4_level(int q) {
-  float v = kNF4[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) v = (q == i) ? kNF4[i] : v;
-  return v;
-}
-
 struct GemvArgs {
   const uint16_t* X;
   const uint8_t* codes;
@@ -211,8 +178,7 @@ __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
       // MFMA j takes elements 8j..8j+7 of every lane's packet, for the token
       // operand and the weight operand alike: the sum over k is unchanged
       const u32x4 xv = *reinterpret_cast<const u32x4*>(&sh.x[col * kc + kl + 8 * j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv), dequant8(c[p][j], cs, sh.lv,
-                                                                             sh.lv16),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv), as_bf16x8(dequant_word8(c[p][j], cs, sh.lv, sh.lv16)),
                                                     acc, 0, 0, 0);
     }
   }

@@ -133,3 +133,34 @@ def test_prefill_down_projection_sampled(q):
     _, dAo, dBo = oracle.linear_bwd(dYh, Xh, np.zeros((N, K), np.float32), Ah, Bh, s)
     assert_close(host_f32(dA), dAo, "down dA")
     assert_close(host_f32(dB), dBo, "down dB")
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 256, 512), (64, 384, 320), (160, 192, 640)])
+def test_compute_weight_bit_exact_in_products(q, M, N, K):
+    """One-hot token rows and a zero adapter make every output a single
+    product 1 * bf16(w'): the forward returns Y[m][n] = bf16(w'[n][k_m]) and
+    dX with one-hot dY rows returns bf16(w'[n_m][k]) exactly. This pins the
+    dequantization inside the fused kernels (GEMV for M <= 16, the MFMA
+    contraction otherwise) bit for bit to the oracle's compute weight."""
+    dev = device()
+    print(f"[case] one-hot compute weight M={M} N={N} K={K}", flush=True)
+    r = 8
+    W, _, _, _, _ = synthetic.linear_inputs(M, N, K, r, dev, seed=3, need_dy=False)
+    st = q.qlora_nf4_quantize(W)
+    ref, wp = oracle_wprime(W)
+    wpb = oracle.bf16_round(wp)  # bf16(w') as float values
+    rng = np.random.default_rng(M + N + K)
+    ks = rng.integers(0, K, size=M)
+    X = torch.zeros(M, K, dtype=torch.bfloat16, device=dev)
+    X[torch.arange(M), torch.as_tensor(ks, device=dev)] = 1.0
+    A = torch.zeros(K, r, dtype=torch.bfloat16, device=dev)
+    B = torch.zeros(r, N, dtype=torch.bfloat16, device=dev)
+    Y, T = q.qlora_linear_fwd(X, st, A, B, 2.0)
+    ns = rng.integers(0, N, size=M)
+    dY = torch.zeros(M, N, dtype=torch.bfloat16, device=dev)
+    dY[torch.arange(M), torch.as_tensor(ns, device=dev)] = 1.0
+    dX, dA, dB = q.qlora_linear_bwd(dY, X, T, st, A, B, 2.0)
+    torch.cuda.synchronize()
+    Yh, dXh = host_f32(Y), host_f32(dX)
+    np.testing.assert_array_equal(Yh, wpb[:, ks].T.astype(np.float32), err_msg="forward weights")
+    np.testing.assert_array_equal(dXh, wpb[ns, :].astype(np.float32), err_msg="dX weights")
