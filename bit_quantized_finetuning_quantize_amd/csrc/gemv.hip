@@ -15,7 +15,8 @@
 //    k of one row, inside one 64-block) and the few dword loads that hold
 //    their 8-bit and second-level constants, while the workgroup stages the
 //    split's token rows in LDS. It then dequantizes each packet in registers
-//    (level tables and the fl(q8/255) table in LDS) straight into the B
+//    (v_perm_b32 byte selection from the block's 16 possible weights, the
+//    fl(q8/255) table in LDS) straight into the B
 //    operand of v_mfma_f32_16x16x32_bf16, with the tokens as the A operand
 //    (rows >= M are zero). The contraction index inside one MFMA is permuted
 //    identically for both operands, which leaves the sum unchanged. The k
@@ -69,8 +70,6 @@ struct alignas(16) Shared {
   static constexpr int kX = 16 * I * kChunk;   // token rows [16][kc] bf16
   static constexpr int kA = kTK * kTCols;      // adapter chunk [512][64] bf16
   static constexpr int kU16 = kX > kA ? kX : kA;
-  float lv[16];
-  float lv16[64];    // level q at lv16[4 q] (16-byte stride)
   float l8[256];
   union {
     uint16_t x[kU16];
@@ -148,10 +147,6 @@ __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
   const float s2b = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)((g0 + 1) * 4) : kOut, 0, 0));
   // lookup tables, built while the loads are in flight
-  if (tid < 16) {
-    sh.lv[tid] = nf4_level(tid);
-    sh.lv16[4 * tid] = nf4_level(tid);
-  }
   if (tid < 256) {
 #pragma clang fp contract(off)
     sh.l8[tid] = static_cast<float>(tid) / 255.0f;  // IEEE division
@@ -173,12 +168,14 @@ __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
     const float s2 = (b / kGroup == g0) ? s2a : s2b;
     const float cs = sh.l8[q8] * s2;
     const int kl = kw + p * kChunk + 32 * g;  // this lane's k inside the split
+    const PermTable pt = perm_table(cs);  // lookups by v_perm: no LDS round trips
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // MFMA j takes elements 8j..8j+7 of every lane's packet, for the token
       // operand and the weight operand alike: the sum over k is unchanged
       const u32x4 xv = *reinterpret_cast<const u32x4*>(&sh.x[col * kc + kl + 8 * j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv), as_bf16x8(dequant_word8(c[p][j], cs, sh.lv, sh.lv16)),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv),
+                                                    as_bf16x8(dequant_word_perm(c[p][j], pt)),
                                                     acc, 0, 0, 0);
     }
   }
