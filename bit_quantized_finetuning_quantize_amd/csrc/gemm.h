@@ -34,8 +34,16 @@ namespace gemm {
 constexpr int kStep = 64;                 // contraction elements per step
 constexpr int kRowBytes = 128;            // one LDS tile row
 constexpr int kStages = 3;
-constexpr int kThreads = 512;             // 4 consumer + 4 producer waves
-constexpr int kProducerThreads = 256;
+constexpr int kProducerThreads = 256;     // 4 producer waves
+// Consumer waves per workgroup: 8 (two per SIMD, 64x64 each) for the
+// forward's 256-row tiles, whose B loader (Nf4Rows) asks for them: one
+// wave's matrix work then covers the other's fragment reads after each
+// barrier. 4 (128x64 each) otherwise: the input-gradient kernel measured
+// faster with fewer LDS reads, and the low-rank tiles are small.
+template <int PT, class LB>
+constexpr int cons_waves() { return (PT >= 256 && LB::kWideConsumers) ? 8 : 4; }
+template <int PT, class LB>
+constexpr int threads_for() { return cons_waves<PT, LB>() * 64 + kProducerThreads; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -97,6 +105,7 @@ struct Tables {
 // segment must be a multiple of 64.
 template <int R>
 struct DirectRows {
+  static constexpr bool kWideConsumers = false;
   static constexpr int kDirect = R / 32;  // 1 KiB (8 rows) per instruction
   static constexpr int kRegLoads = 0;
   const uint16_t* base;
@@ -134,6 +143,7 @@ struct DirectRows {
 // columns. Source rows at or past `rows` read as zero.
 template <int R>
 struct ColsBf16 {
+  static constexpr bool kWideConsumers = false;
   static constexpr int kUnits = R * 2;
   static constexpr int kPer = (kUnits + kProducerThreads - 1) / kProducerThreads;
   static constexpr int kDirect = 0;
@@ -192,6 +202,7 @@ struct ColsBf16 {
 // row. Two producer threads per row, 32 codes each.
 template <int R>
 struct Nf4Rows {
+  static constexpr bool kWideConsumers = true;
   static_assert(R * 2 == kProducerThreads, "two producer threads per row");
   static constexpr int kDirect = 0;
   static constexpr int kRegLoads = 3;
@@ -245,6 +256,7 @@ struct Nf4Rows {
 // 128-byte LDS row, so the transposition costs no bank conflicts.
 template <int R>
 struct Nf4Cols {
+  static constexpr bool kWideConsumers = false;
   static_assert(R == 128, "four producer waves x 32 tile rows");
   static constexpr int kDirect = 0;
   static constexpr int kRegLoads = 3;
@@ -305,6 +317,7 @@ struct Nf4Cols {
 
 // A segment that is never used.
 struct LoadNone {
+  static constexpr bool kWideConsumers = false;
   static constexpr int kDirect = 0;
   static constexpr int kRegLoads = 0;
   struct Regs {};
@@ -337,9 +350,9 @@ struct EpiPartial {
 
 // ---------------------------------------------------------------------------
 // Consumer: one 64-wide contraction step on the LDS tiles.
-template <int PT, int QT>
+template <int PT, int QT, int CW>
 struct Consumer {
-  static constexpr int WP = PT / 2, WQ = QT / 2;   // wave tile
+  static constexpr int WP = PT / (CW / 2), WQ = QT / 2;   // wave tile
   static constexpr int BP = WP / 32, BQ = WQ / 32; // 32x32 MFMA blocks per wave
   floatx16 acc[BP][BQ];
   int a_off[4], b_off[4];  // per-lane LDS byte offsets of sub-step kk, block 0
@@ -431,10 +444,12 @@ constexpr size_t lds_bytes() {  // dynamic LDS: the stage ring
   return (size_t)kStages * (PT + QT) * kRowBytes;
 }
 
-// One 512-thread workgroup per compute unit (the LDS ring takes most of the
-// 160 KiB), i.e. two waves per SIMD: let the register allocator use that.
+// One workgroup per compute unit (the LDS ring takes most of the 160 KiB),
+// i.e. two or three waves per SIMD: let the register allocator use that.
 template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__((threads_for<PT, LB1>()))
+    __attribute__((amdgpu_waves_per_eu((threads_for<PT, LB1>() / 256),
+                                       (threads_for<PT, LB1>() / 256))))
 contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // lookup tables at fixed LDS addresses (the compiler folds them into the
@@ -480,13 +495,16 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   // between their MFMAs, and the producers keep the register path.
   constexpr bool kConsA = LA1::kDirect > 0 && LA1::kRegLoads == 0;
 
-  if (wave < 4) {
-    // consumers: n steps, one barrier before each
-    Consumer<PT, QT> cons;
+  constexpr int kCW = cons_waves<PT, LB1>();
+  if (wave < kCW) {
+    // consumers: n steps, one barrier before each. The first four waves
+    // (256 threads) also move the A operand of seg1.
+    Consumer<PT, QT, kCW> cons;
     cons.init(wave, lane);
     LA1 a1 = cfg.a1;
+    const bool mover = wave < 4;
     if constexpr (kConsA) {
-      if (n1 > 0) {
+      if (mover && n1 > 0) {
         a1.setup((int64_t)pt * PT, tid);
         a1.direct(g0, stage(0), tid);
         if (n1 > 1) a1.direct(g0 + 1, stage(1), tid);
@@ -495,14 +513,14 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
     for (int it = 0; it < n; ++it) {
       if constexpr (kConsA) {
         // this wave's A loads of step it have landed (those of it+1 may fly)
-        if (it + 1 < n1) wait_vmcnt<LA1::kDirect>();
-        else if (it < n1) wait_vmcnt<0>();
+        if (mover && it + 1 < n1) wait_vmcnt<LA1::kDirect>();
+        else if (mover && it < n1) wait_vmcnt<0>();
       }
       stage_barrier();  // stage it % 3 written
       // stage (it+2) % 3 was last read in step it-1, which every consumer
       // finished before this barrier
       if constexpr (kConsA) {
-        if (it + 2 < n1) a1.direct(g0 + it + 2, stage(it + 2), tid);
+        if (mover && it + 2 < n1) a1.direct(g0 + it + 2, stage(it + 2), tid);
       }
       const uint32_t sA = stage(it);
       cons.step(sA, sA + kBOff);
@@ -518,7 +536,7 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
   if (n == 0) return;
 
   // ---- producers: exactly n barriers, one after each produced step ----
-  const int t = tid - kProducerThreads;
+  const int t = tid - kCW * 64;
   const Tables tb{s_lv, s_lv16, s_l8};
 
   LA2 a2 = cfg.a2; LB2 b2 = cfg.b2;

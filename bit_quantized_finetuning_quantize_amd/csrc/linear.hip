@@ -183,7 +183,7 @@ hipError_t run(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg, hipStream_t str
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)cfg.nP * cfg.nQ * cfg.splits;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, stream, cfg);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads_for<PT, LB1>()), lds, stream, cfg);
   return hipGetLastError();
 }
 
