@@ -447,10 +447,8 @@ constexpr size_t lds_bytes() {  // dynamic LDS: the stage ring
 // One workgroup per compute unit (the LDS ring takes most of the 160 KiB),
 // i.e. two or three waves per SIMD: let the register allocator use that.
 template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
-__global__ void __launch_bounds__((threads_for<PT, LB1>()))
-    __attribute__((amdgpu_waves_per_eu((threads_for<PT, LB1>() / 256),
-                                       (threads_for<PT, LB1>() / 256))))
-contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
+__device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi>& cfg,
+                                                 int block) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // lookup tables at fixed LDS addresses (the compiler folds them into the
   // instruction offsets); the dynamic LDS holds the stage ring
@@ -475,7 +473,7 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
     s_lv16[4 * tid] = nf4_level(tid);
   }
 
-  int id = blockIdx.x;
+  int id = block;
   const int pt = id % cfg.nP; id /= cfg.nP;
   const int qt = id % cfg.nQ; id /= cfg.nQ;
   const int split = id;
@@ -603,6 +601,28 @@ contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
     stage_barrier();
   }
   wait_vmcnt<0>();  // no direct load may outlive the workgroup's LDS
+}
+
+template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
+__global__ void __launch_bounds__((threads_for<PT, LB1>()))
+    __attribute__((amdgpu_waves_per_eu((threads_for<PT, LB1>() / 256),
+                                       (threads_for<PT, LB1>() / 256))))
+contraction_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg) {
+  contraction_body<PT, QT, LA1, LB1, LA2, LB2, Epi, kPartial>(cfg, blockIdx.x);
+}
+
+// Two independent contractions of one shape in one launch: workgroups
+// [0, nb0) run c0, the rest run c1.
+template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
+__global__ void __launch_bounds__((threads_for<PT, LB1>()))
+    __attribute__((amdgpu_waves_per_eu((threads_for<PT, LB1>() / 256),
+                                       (threads_for<PT, LB1>() / 256))))
+contraction_pair_kernel(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> c0,
+                        Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> c1, int nb0) {
+  if ((int)blockIdx.x < nb0)
+    contraction_body<PT, QT, LA1, LB1, LA2, LB2, Epi, kPartial>(c0, blockIdx.x);
+  else
+    contraction_body<PT, QT, LA1, LB1, LA2, LB2, Epi, kPartial>(c1, blockIdx.x - nb0);
 }
 
 }  // namespace gemm

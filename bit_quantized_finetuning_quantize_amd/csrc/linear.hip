@@ -24,6 +24,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace qlora {
 
@@ -34,10 +35,11 @@ namespace {
 constexpr int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Number of contraction splits for a split-K launch: about two workgroups
-// per compute unit, at least two steps per split.
+// Number of contraction splits for a split-K launch: about one workgroup per
+// compute unit (measured faster than two: fewer partials to write and sum),
+// at least two steps per split.
 int64_t choose_splits(int64_t tiles, int64_t steps) {
-  int64_t want = ceil_div(512, std::max<int64_t>(tiles, 1));
+  int64_t want = ceil_div(256, std::max<int64_t>(tiles, 1));
   int64_t maxs = std::max<int64_t>(1, steps / 2);
   int64_t s = std::min(want, maxs);
   if (s < 1) s = 1;
@@ -45,11 +47,16 @@ int64_t choose_splits(int64_t tiles, int64_t steps) {
   return ceil_div(steps, per);
 }
 
+// Split count shared by the dA and dB^T contractions of one launch.
+int64_t grad_splits(int64_t M, int64_t N, int64_t K, int64_t r64) {
+  return choose_splits((ceil_div(K, 128) + ceil_div(N, 128)) * (r64 / 64), ceil_div(M, 64));
+}
+
 // ---------------------------------------------------------------------------
 // workspace carve-up (byte offsets, 256-aligned)
 struct WsLayout {
   int64_t r64, Mp;
-  size_t apad, at, t32, st, stt, g32, sg, sgt, part, total;
+  size_t apad, at, t32, st, stt, sg, sgt, part, total;
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -63,7 +70,6 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   w.t32 = take((size_t)M * r * 4);
   w.st = take((size_t)w.Mp * w.r64 * 2);
   w.stt = take((size_t)w.r64 * w.Mp * 2);
-  w.g32 = take((size_t)M * r * 4);
   w.sg = take((size_t)w.Mp * w.r64 * 2);
   w.sgt = take((size_t)w.r64 * w.Mp * 2);
   // split-K partials: the largest of the four low-rank contractions
@@ -73,8 +79,14 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   };
   consider(M, w.r64, choose_splits(ceil_div(M, 64) * (w.r64 / 64), ceil_div(K, 64)));
   consider(M, w.r64, choose_splits(ceil_div(M, 64) * (w.r64 / 64), ceil_div(N, 64)));
-  consider(K, w.r64, choose_splits(ceil_div(K, 128) * (w.r64 / 64), ceil_div(M, 64)));
-  consider(w.r64, N, choose_splits((w.r64 / 64) * ceil_div(N, 128), ceil_div(M, 64)));
+  {  // dA and dB^T partials side by side (one launch, common split count s).
+     // With t tiles, s <= 256 / t + 1 and t >= (K + N) r64 / (128 * 64), so
+     // the bound below holds for every s and grows with K and N: a workspace
+     // sized for the largest shape serves the smaller ones.
+    const int64_t sp = grad_splits(M, N, K, w.r64);
+    const int64_t bound = 256 * 128 * 64 + (K + N) * w.r64;
+    pe = std::max(pe, (size_t)std::max((K + N) * w.r64 * sp, bound));
+  }
   // the small-M forward path keeps its own partials here too
   pe = std::max(pe, (size_t)gemv_partial_elems(M, N, K, r));
   w.part = take(pe * 4);
@@ -96,12 +108,13 @@ template __global__ void contraction_kernel<256, 128, DirectRows<256>, Nf4Cols<1
 template __global__ void contraction_kernel<64, 64, DirectRows<64>, DirectRows<64>, LoadNone,
     LoadNone, EpiPartial, true>(
     Contraction<64, 64, DirectRows<64>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>);
-template __global__ void contraction_kernel<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone,
+template __global__ void contraction_kernel<64, 64, DirectRows<64>, ColsBf16<64>, LoadNone,
     LoadNone, EpiPartial, true>(
-    Contraction<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>);
-template __global__ void contraction_kernel<64, 128, DirectRows<64>, ColsBf16<128>, LoadNone,
+    Contraction<64, 64, DirectRows<64>, ColsBf16<64>, LoadNone, LoadNone, EpiPartial>);
+template __global__ void contraction_pair_kernel<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone,
     LoadNone, EpiPartial, true>(
-    Contraction<64, 128, DirectRows<64>, ColsBf16<128>, LoadNone, LoadNone, EpiPartial>);
+    Contraction<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>,
+    Contraction<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>, int);
 }  // namespace gemm
 
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
@@ -153,17 +166,38 @@ __global__ void reduce_lowrank_kernel(const float* __restrict__ part, int splits
   }
 }
 
-// out[p][q] = sum_s part[s][p][q] for p < Pv, q < Qv (partials dense P x Q).
-__global__ void reduce_plain_kernel(const float* __restrict__ part, int splits, int64_t P,
-                                    int64_t Q, int64_t Pv, int64_t Qv,
-                                    float* __restrict__ out, int64_t ldo) {
-  const int64_t total = Pv * Qv;
+// Adapter gradients from their split partials, summed in split order:
+//   dA[k][j] = sum_s pa[s][k][j]        (pa dense [splits][K][r64])
+//   dB[j][n] = sum_s pb[s][n][j]        (pb dense [splits][N][r64], dB^T)
+// One thread per four columns of a partial row (k, then n): consecutive
+// threads read consecutive 16-byte pieces of a row.
+__global__ void reduce_grads_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
+                                    int splits, int64_t K, int64_t N, int r, int64_t r64,
+                                    float* __restrict__ dA, float* __restrict__ dB) {
+  const int64_t per_row = r64 / 4;
+  const int64_t total = (K + N) * per_row;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p = i / Qv, q = i % Qv;
-    float v = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * P + p) * Q + q];
-    out[p * ldo + q] = v;
+    const int64_t row = i / per_row;
+    const int j0 = (int)(i % per_row) * 4;
+    if (j0 >= r) continue;
+    const bool is_a = row < K;
+    const int64_t p = is_a ? row : row - K;
+    const int64_t P = is_a ? K : N;
+    const float* part = is_a ? pa : pb;
+    floatx4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < splits; ++sp) {
+      const floatx4 u = *reinterpret_cast<const floatx4*>(part + ((int64_t)sp * P + p) * r64 + j0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] += u[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (j0 + c < r) {
+        if (is_a) dA[p * r + j0 + c] = v[c];
+        else dB[(int64_t)(j0 + c) * N + p] = v[c];
+      }
+    }
   }
 }
 
@@ -175,15 +209,44 @@ unsigned grid_for(int64_t total, int threads = 256) {
 // ---------------------------------------------------------------------------
 // launching a contraction
 
+// Dynamic LDS above the default limit: raised once per device and kernel
+// (the flag is per kernel instantiation), not on every launch.
+template <class Kern>
+hipError_t raise_lds_limit(Kern kern, size_t lds) {
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (raised.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) raised.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
 hipError_t run(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> cfg, hipStream_t stream) {
   auto kern = contraction_kernel<PT, QT, LA1, LB1, LA2, LB2, Epi, kPartial>;
   const size_t lds = lds_bytes<PT, QT>();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = raise_lds_limit(kern, lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)cfg.nP * cfg.nQ * cfg.splits;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads_for<PT, LB1>()), lds, stream, cfg);
+  return hipGetLastError();
+}
+
+template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi, bool kPartial>
+hipError_t run_pair(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> c0,
+                    Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> c1, hipStream_t stream) {
+  auto kern = contraction_pair_kernel<PT, QT, LA1, LB1, LA2, LB2, Epi, kPartial>;
+  const size_t lds = lds_bytes<PT, QT>();
+  hipError_t e = raise_lds_limit(kern, lds);
+  if (e != hipSuccess) return e;
+  const int64_t nb0 = (int64_t)c0.nP * c0.nQ * c0.splits;
+  const int64_t nb1 = (int64_t)c1.nP * c1.nQ * c1.splits;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(nb0 + nb1)), dim3(threads_for<PT, LB1>()), lds, stream,
+                     c0, c1, (int)nb0);
   return hipGetLastError();
 }
 
@@ -220,8 +283,15 @@ hipError_t lowrank_partials(const uint16_t* a, int64_t lda, int64_t M, int64_t C
     if (e_ != hipSuccess) return e_;       \
   } while (0)
 
+// The adapter can be read in place when its rows are whole 64-column tiles
+// and 16-byte aligned: no padded copy, no transposed copy.
+bool adapter_in_place(const uint16_t* A, int r) {
+  return r % 64 == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+}
+
 hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, char* ws,
                         hipStream_t stream) {
+  if (adapter_in_place(A, r)) return hipSuccess;
   hipLaunchKernelGGL(adapter_prep_kernel, dim3(grid_for(K * w.r64)), dim3(256), 0, stream, A, K,
                      r, w.r64, reinterpret_cast<uint16_t*>(ws + w.apad),
                      reinterpret_cast<uint16_t*>(ws + w.at));
@@ -229,14 +299,20 @@ hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, 
 }
 
 // T = X A -> out32 (optional), bf16(s T) [Mp x r64], bf16(s T)^T (optional).
-hipError_t compute_T(const uint16_t* X, const uint16_t* At, int64_t M, int64_t K, int r,
+hipError_t compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
                      const WsLayout& w, char* ws, float s, float* out32, bool transposed,
                      hipStream_t stream) {
   float* part = reinterpret_cast<float*>(ws + w.part);
   int splits = 0;
-  // Bop[j][k] = A^T[j][k]: rows of the transposed, padded adapter
-  DirectRows<64> lb{At, K, w.r64};
-  QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
+  if (adapter_in_place(A, r)) {
+    // Bop[j][k] = A[k][j]: columns of the adapter, transposed on the way in
+    ColsBf16<64> lb{A, (int64_t)r, K, (int64_t)r};
+    QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
+  } else {
+    // Bop[j][k] = A^T[j][k]: rows of the transposed, padded adapter copy
+    DirectRows<64> lb{reinterpret_cast<const uint16_t*>(ws + w.at), K, w.r64};
+    QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
+  }
   hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
                      part, splits, w.r64, M, r, w.r64, w.Mp, s, out32,
                      reinterpret_cast<uint16_t*>(ws + w.st),
@@ -253,9 +329,8 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
   QLORA_TRY(prep_adapter(A, K, r, w, ws, stream));
-  const uint16_t* at = reinterpret_cast<const uint16_t*>(ws + w.at);
   float* t32 = T_out ? T_out : reinterpret_cast<float*>(ws + w.t32);
-  QLORA_TRY(compute_T(X, at, M, K, r, w, ws, scale, t32, false, stream));
+  QLORA_TRY(compute_T(X, A, M, K, r, w, ws, scale, t32, false, stream));
 
   using LA1 = DirectRows<256>;
   using LB1 = Nf4Rows<128>;
@@ -286,8 +361,8 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   const WsLayout w = ws_layout(M, N, K, r);
   float* part = reinterpret_cast<float*>(ws + w.part);
   QLORA_TRY(prep_adapter(A, K, r, w, ws, stream));
-  const uint16_t* apad = reinterpret_cast<const uint16_t*>(ws + w.apad);
-  const uint16_t* at = reinterpret_cast<const uint16_t*>(ws + w.at);
+  const uint16_t* apad =
+      adapter_in_place(A, r) ? A : reinterpret_cast<const uint16_t*>(ws + w.apad);
 
   // 1. G = dY B^T  (Bop[j][n] = B[j][n], rows j < r)
   {
@@ -295,8 +370,7 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
     DirectRows<64> lb{B, N, (int64_t)r};
     QLORA_TRY(lowrank_partials(dY, N, M, N, lb, w.r64, part, &splits, stream));
     hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
-                       part, splits, w.r64, M, r, w.r64, w.Mp, scale,
-                       reinterpret_cast<float*>(ws + w.g32),
+                       part, splits, w.r64, M, r, w.r64, w.Mp, scale, (float*)nullptr,
                        reinterpret_cast<uint16_t*>(ws + w.sg),
                        reinterpret_cast<uint16_t*>(ws + w.sgt));
     QLORA_TRY(hipGetLastError());
@@ -309,7 +383,7 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
                        reinterpret_cast<uint16_t*>(ws + w.stt));
     QLORA_TRY(hipGetLastError());
   } else {
-    QLORA_TRY(compute_T(X, at, M, K, r, w, ws, scale, reinterpret_cast<float*>(ws + w.t32),
+    QLORA_TRY(compute_T(X, A, M, K, r, w, ws, scale, reinterpret_cast<float*>(ws + w.t32),
                         true, stream));
   }
   // 3. dX = dY W' + (s G) A^T
@@ -334,36 +408,36 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
     QLORA_TRY((run<256, 128, LA1, LB1, LA2, LB2, EpiBf16, false>(cfg, stream)));
     QLORA_TRY(record_if(ev1, stream));
   }
-  // 4a. dA = X^T (s G): P = K, Q = r64, contraction over M
+  // 4. dA = X^T (s G) (P = K) and dB^T = dY^T (s T) (P = N): Q = r64,
+  //    contraction over M, one launch for both, then one reduce
   {
-    using LA = ColsBf16<128>;    // Aop[k][m] = X[m][k]
-    using LB = DirectRows<64>;   // Bop[j][m] = (sG)^T[j][m]
-    Contraction<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial> cfg{};
-    cfg.a1 = LA{X, K, M, K};
-    cfg.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.sgt), w.Mp, w.r64};
-    cfg.nP = (int)ceil_div(K, 128);
-    cfg.nQ = (int)(w.r64 / 64);
-    set_steps(cfg, ceil_div(M, 64), 0, (int64_t)cfg.nP * cfg.nQ);
-    cfg.epi = EpiPartial{part, K, w.r64};
-    QLORA_TRY((run<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial, true>(cfg, stream)));
-    hipLaunchKernelGGL(reduce_plain_kernel, dim3(grid_for(K * r)), dim3(256), 0, stream, part,
-                       cfg.splits, K, w.r64, K, (int64_t)r, dA, (int64_t)r);
-    QLORA_TRY(hipGetLastError());
-  }
-  // 4b. dB = (s T)^T dY: P = r64, Q = N, contraction over M
-  {
-    using LA = DirectRows<64>;   // Aop[j][m] = (sT)^T[j][m]
-    using LB = ColsBf16<128>;    // Bop[n][m] = dY[m][n]
-    Contraction<64, 128, LA, LB, LoadNone, LoadNone, EpiPartial> cfg{};
-    cfg.a1 = LA{reinterpret_cast<const uint16_t*>(ws + w.stt), w.Mp, w.r64};
-    cfg.b1 = LB{dY, N, M, N};
-    cfg.nP = (int)(w.r64 / 64);
-    cfg.nQ = (int)ceil_div(N, 128);
-    set_steps(cfg, ceil_div(M, 64), 0, (int64_t)cfg.nP * cfg.nQ);
-    cfg.epi = EpiPartial{part, w.r64, N};
-    QLORA_TRY((run<64, 128, LA, LB, LoadNone, LoadNone, EpiPartial, true>(cfg, stream)));
-    hipLaunchKernelGGL(reduce_plain_kernel, dim3(grid_for((int64_t)r * N)), dim3(256), 0, stream,
-                       part, cfg.splits, w.r64, N, (int64_t)r, N, dB, N);
+    using LA = ColsBf16<128>;    // Aop[k][m] = X[m][k], Aop[n][m] = dY[m][n]
+    using LB = DirectRows<64>;   // Bop[j][m] = (sG)^T[j][m], (sT)^T[j][m]
+    using C = Contraction<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial>;
+    const int64_t splits = grad_splits(M, N, K, w.r64);
+    const int64_t steps = ceil_div(M, 64);
+    float* pa = part;
+    float* pb = part + K * w.r64 * splits;
+    C ca{}, cb{};
+    ca.a1 = LA{X, K, M, K};
+    ca.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.sgt), w.Mp, w.r64};
+    ca.nP = (int)ceil_div(K, 128);
+    ca.epi = EpiPartial{pa, K, w.r64};
+    cb.a1 = LA{dY, N, M, N};
+    cb.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.stt), w.Mp, w.r64};
+    cb.nP = (int)ceil_div(N, 128);
+    cb.epi = EpiPartial{pb, N, w.r64};
+    for (C* c : {&ca, &cb}) {
+      c->nQ = (int)(w.r64 / 64);
+      c->S1 = (int)steps;
+      c->S2 = 0;
+      c->steps_per_split = (int)ceil_div(steps, splits);
+      c->splits = (int)ceil_div(steps, c->steps_per_split);
+    }
+    QLORA_TRY((run_pair<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial, true>(ca, cb, stream)));
+    hipLaunchKernelGGL(reduce_grads_kernel, dim3(grid_for((K + N) * (w.r64 / 4))), dim3(256), 0,
+                       stream, pa, pb,
+                       ca.splits, K, N, r, w.r64, dA, dB);
     QLORA_TRY(hipGetLastError());
   }
   return hipSuccess;
