@@ -15,7 +15,8 @@
 // Backward:
 //   1. G = dY B^T         split-K contraction -> reduce (fp32 G, bf16 s G,
 //                         bf16 (s G)^T)
-//   2. T (recomputed when the caller passes none) and bf16 (s T)^T
+//   2. bf16 (s T)^T from T (in the same reduce launch), or T recomputed
+//      when the caller passes none
 //   3. dX = dY W' + (sG) A^T   one contraction over N + r; the weight tile is
 //                         dequantized and transposed into LDS
 //   4. dA = X^T (sG),  dB = (sT)^T dY   split-M contractions -> reduce
@@ -145,24 +146,36 @@ hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, 
 
 // Reduce split-K partials of an [M x r] low-rank product (partial layout
 // [split][M][ld]) and emit: float32 V (optional), bf16(s V) padded
-// [Mp x r64] and its transpose [r64 x Mp] (optional).
-__global__ void reduce_lowrank_kernel(const float* __restrict__ part, int splits,
-                                      int64_t ld, int64_t M, int r, int64_t r64,
-                                      int64_t Mp, float s, float* __restrict__ out32,
-                                      uint16_t* __restrict__ sv,
-                                      uint16_t* __restrict__ svt) {
-  const int64_t total = Mp * r64;
+// [Mp x r64] (optional) and its transpose [r64 x Mp] (optional).
+struct LowrankJob {
+  const float* part;
+  int splits;
+  int64_t ld;
+  float* out32;
+  uint16_t* sv;
+  uint16_t* svt;
+};
+
+// One or two jobs of the same shape in one launch (the second one when
+// jobs[1].part is set): elements [0, Mp r64) are job 0's, the rest job 1's.
+__global__ void reduce_lowrank_kernel(LowrankJob j0, LowrankJob j1, int64_t M, int r,
+                                      int64_t r64, int64_t Mp, float s) {
+  const int64_t per = Mp * r64;
+  const int64_t total = j1.part ? 2 * per : per;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / r64, j = i % r64;
+    const bool second = i >= per;
+    const LowrankJob& jb = second ? j1 : j0;
+    const int64_t e = second ? i - per : i;
+    const int64_t m = e / r64, j = e % r64;
     float v = 0.0f;
     if (m < M && j < r) {
-      for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * M + m) * ld + j];
-      if (out32) out32[m * r + j] = v;
+      for (int sp = 0; sp < jb.splits; ++sp) v += jb.part[((int64_t)sp * M + m) * jb.ld + j];
+      if (jb.out32) jb.out32[m * r + j] = v;
     }
     const uint16_t b = (uint16_t)(pack_bf16x2(s * v, 0.0f) & 0xffffu);
-    sv[i] = b;
-    if (svt) svt[j * Mp + m] = b;
+    if (jb.sv) jb.sv[e] = b;
+    if (jb.svt) jb.svt[j * Mp + m] = b;
   }
 }
 
@@ -313,10 +326,10 @@ hipError_t compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K,
     DirectRows<64> lb{reinterpret_cast<const uint16_t*>(ws + w.at), K, w.r64};
     QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
   }
+  const LowrankJob jt{part, splits, w.r64, out32, reinterpret_cast<uint16_t*>(ws + w.st),
+                      transposed ? reinterpret_cast<uint16_t*>(ws + w.stt) : nullptr};
   hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
-                     part, splits, w.r64, M, r, w.r64, w.Mp, s, out32,
-                     reinterpret_cast<uint16_t*>(ws + w.st),
-                     transposed ? reinterpret_cast<uint16_t*>(ws + w.stt) : nullptr);
+                     jt, LowrankJob{}, M, r, w.r64, w.Mp, s);
   return hipGetLastError();
 }
 
@@ -364,25 +377,22 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   const uint16_t* apad =
       adapter_in_place(A, r) ? A : reinterpret_cast<const uint16_t*>(ws + w.apad);
 
-  // 1. G = dY B^T  (Bop[j][n] = B[j][n], rows j < r)
+  // 1. G = dY B^T  (Bop[j][n] = B[j][n], rows j < r), reduced together with
+  // 2. bf16 (s T)^T from the caller's T (or T recomputed when there is none)
   {
     int splits = 0;
     DirectRows<64> lb{B, N, (int64_t)r};
     QLORA_TRY(lowrank_partials(dY, N, M, N, lb, w.r64, part, &splits, stream));
-    hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
-                       part, splits, w.r64, M, r, w.r64, w.Mp, scale, (float*)nullptr,
-                       reinterpret_cast<uint16_t*>(ws + w.sg),
-                       reinterpret_cast<uint16_t*>(ws + w.sgt));
+    const LowrankJob jg{part, splits, w.r64, nullptr, reinterpret_cast<uint16_t*>(ws + w.sg),
+                        reinterpret_cast<uint16_t*>(ws + w.sgt)};
+    const LowrankJob jt = T ? LowrankJob{T, 1, (int64_t)r, nullptr, nullptr,
+                                         reinterpret_cast<uint16_t*>(ws + w.stt)}
+                            : LowrankJob{};
+    hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for((T ? 2 : 1) * w.Mp * w.r64)),
+                       dim3(256), 0, stream, jg, jt, M, r, w.r64, w.Mp, scale);
     QLORA_TRY(hipGetLastError());
   }
-  // 2. bf16 (s T)^T, recomputing T if needed
-  if (T) {
-    hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
-                       T, 1, (int64_t)r, M, r, w.r64, w.Mp, scale, (float*)nullptr,
-                       reinterpret_cast<uint16_t*>(ws + w.st),
-                       reinterpret_cast<uint16_t*>(ws + w.stt));
-    QLORA_TRY(hipGetLastError());
-  } else {
+  if (!T) {
     QLORA_TRY(compute_T(X, A, M, K, r, w, ws, scale, reinterpret_cast<float*>(ws + w.t32),
                         true, stream));
   }
