@@ -344,9 +344,9 @@ def run_gemv(args, q, synthetic, torch, dev):
 
 def cpu_baseline(args, projs, torch):
     """The oracle, timed on this host on a bounded sample: forward and
-    backward of the gate projection (11008x4096, r=64) for the first
-    `cpu_rows` tokens, including its dequantization of the weight; the
-    weight is quantized by the oracle before timing."""
+    backward of the three projections, r=64, for the first `cpu_rows` tokens
+    each, `cpu_reps` times, including the dequantization of each weight; the
+    weights are quantized by the oracle before timing."""
     import numpy as np
     import oracle
     try:
@@ -354,24 +354,30 @@ def cpu_baseline(args, projs, torch):
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    p = projs[0]
     Mc = args.cpu_rows
-    r = p["A"].shape[1]
     f = lambda t: t.detach().float().cpu().numpy()
-    W = f(p["W"]).ravel()
-    X, A, B, dY = f(p["X"][:Mc]), f(p["A"]), f(p["B"]), f(p["dY"][:Mc])
-    ref = oracle.quantize(W)
-    N, K = p["N"], p["K"]
-    t0 = time.perf_counter()
-    wp = oracle.dequantize(ref["codes"], ref["absmax_q"], ref["absmax_s2"], N * K).reshape(N, K)
-    oracle.linear_fwd(X, wp, A, B, 0.25)
-    oracle.linear_bwd(dY, X, wp, A, B, 0.25)
-    dt = time.perf_counter() - t0
-    flops = 4 * Mc * N * K + 6 * Mc * r * (K + N)
+    prepared = []
+    for p in projs:
+        W = f(p["W"]).ravel()
+        prepared.append((p, oracle.quantize(W), f(p["X"][:Mc]), f(p["A"]), f(p["B"]),
+                         f(p["dY"][:Mc])))
+    flops, dt = 0, 0.0
+    for _ in range(args.cpu_reps):
+        for p, ref, X, A, B, dY in prepared:
+            r = A.shape[1]
+            N, K = p["N"], p["K"]
+            t0 = time.perf_counter()
+            wp = oracle.dequantize(ref["codes"], ref["absmax_q"], ref["absmax_s2"],
+                                   N * K).reshape(N, K)
+            oracle.linear_fwd(X, wp, A, B, 0.25)
+            oracle.linear_bwd(dY, X, wp, A, B, 0.25)
+            dt += time.perf_counter() - t0
+            flops += 4 * Mc * N * K + 6 * Mc * r * (K + N)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"gate projection 11008x4096, r=64, first {Mc} of 2048 tokens: "
-                      f"dequantize + forward + backward in float64 numpy ({dt:.2f} s)"}
+            "sample": f"the three projections (gate, up, down), r=64, first {Mc} of 2048 tokens "
+                      f"each, {args.cpu_reps} times: dequantize + forward + backward in float64 "
+                      f"numpy ({dt:.2f} s)"}
 
 
 def main():
@@ -381,7 +387,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--gemv-stores", type=int, default=64)
     ap.add_argument("--gemv-rounds", type=int, default=8)
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
