@@ -23,10 +23,16 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kRounds = kGroup * kBlock / (kQuantThreads * 8);  // 8
 
-__device__ __forceinline__ uint32_t nf4_index(float n) {
-  uint32_t q = 0;
-#pragma unroll
-  for (int j = 0; j < 15; ++j) q += (n > kThr.t[j]) ? 1u : 0u;
+// The nearest level's index q = #{j : n > thr[j]}, found by a four-step
+// binary search over the 15 sorted thresholds: thr holds them in LDS (its
+// 15 entries sit on 15 different banks, so the lane-varying reads do not
+// conflict). Equal to counting for every n, NaN included (every comparison
+// is false, q = 0).
+__device__ __forceinline__ uint32_t nf4_index(float n, const float* thr) {
+  uint32_t q = (n > kThr.t[7]) ? 8u : 0u;
+  q += (n > thr[q + 3]) ? 4u : 0u;
+  q += (n > thr[q + 1]) ? 2u : 0u;
+  q += (n > thr[q]) ? 1u : 0u;
   return q;
 }
 
@@ -38,8 +44,10 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
 #pragma clang fp contract(off)
   __shared__ float s_blockmax[kGroup];
   __shared__ float s_wavemax[kQuantThreads / 64];
+  __shared__ float s_thr[16];
 
   const int tid = threadIdx.x;
+  if (tid < 15) s_thr[tid] = kThr.t[tid];  // visible after the first barrier
   const int64_t group = blockIdx.x;
   const int64_t gbase = group * (int64_t)(kGroup * kBlock);
   const int64_t nbytes = (numel + 1) / 2;
@@ -111,8 +119,8 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
     for (int i = 0; i < 4; ++i) {
       const float a = bf16_lo(vals[r][i]);
       const float b = bf16_hi(vals[r][i]);
-      uint32_t qa = (c > 0.0f) ? nf4_index(a / c) : 7u;
-      uint32_t qb = (c > 0.0f) ? nf4_index(b / c) : 7u;
+      uint32_t qa = (c > 0.0f) ? nf4_index(a / c, s_thr) : 7u;
+      uint32_t qb = (c > 0.0f) ? nf4_index(b / c, s_thr) : 7u;
       // nibbles past the end of the tensor stay 0
       if (e0 + 2 * i >= numel) qa = 0u;
       if (e0 + 2 * i + 1 >= numel) qb = 0u;
