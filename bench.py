@@ -283,6 +283,21 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     qms = qa.elapsed_time(qb) / 10
     res["quantize"] = dict(shape=[11008, 4096], ms=qms,
                            GBps=(2 * W0.numel() + st0.nbytes()) / (qms * 1e-3) / 1e9)
+    # adapter merge into a bf16 copy of the same weight (store in, bf16 out)
+    A0, B0 = projs[0]["A"], projs[0]["B"]
+    merged = q.qlora_nf4_merge(st0, A0, B0, s)
+    for _ in range(2):
+        q.qlora_nf4_merge(st0, A0, B0, s, out=merged)
+    torch.cuda.synchronize()
+    qa.record()
+    for _ in range(10):
+        q.qlora_nf4_merge(st0, A0, B0, s, out=merged)
+    qb.record()
+    torch.cuda.synchronize()
+    mms = qa.elapsed_time(qb) / 10
+    res["merge"] = dict(shape=[11008, 4096], rank=r, ms=mms,
+                        GBps=(st0.nbytes() + 2 * W0.numel()) / (mms * 1e-3) / 1e9,
+                        rank_flops_TFLOPs=2 * W0.numel() * r / (mms * 1e-3) / 1e12)
     return res, projs
 
 
@@ -470,6 +485,7 @@ def main():
             "avg_launch_ms": round(pre["dx_kernel_ms"], 4),
         },
         "quantize": pre["quantize"],
+        "merge": pre["merge"],
         "gemv": gemv,
         "cpu_baseline": cpu,
     }

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     qlora_nf4_codes_bytes,
     qlora_nf4_dequantize,
     qlora_nf4_dequantize_bf16,
+    qlora_nf4_merge,
     qlora_nf4_num_blocks,
     qlora_nf4_num_groups,
     qlora_nf4_quantize,

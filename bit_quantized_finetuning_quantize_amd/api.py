@@ -101,6 +101,18 @@ def qlora_nf4_dequantize_bf16(st, out=None):
     return out
 
 
+def qlora_nf4_merge(st, A, B, scale, out=None):
+    """bf16(w' + scale (A B)^T) for a store of W [N x K]: the adapter folded
+    into a 16-bit copy of the frozen weight; returns bf16 [N x K]."""
+    N, K = st.shape
+    r = A.shape[1]
+    out = out if out is not None else torch.empty(N, K, dtype=torch.bfloat16,
+                                                  device=st.codes.device)
+    _check(LIB.qlora_nf4_merge(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2), N, K,
+                               _ptr(A), _ptr(B), r, float(scale), _ptr(out), _stream()))
+    return out
+
+
 def qlora_linear_workspace_bytes(M, N, K, r):
     return int(LIB.qlora_linear_workspace_bytes(M, N, K, r))
 

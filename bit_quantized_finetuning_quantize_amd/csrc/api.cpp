@@ -84,6 +84,21 @@ int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
   return dequant_common(codes, absmax_q, absmax_s2, numel, out, true, stream);
 }
 
+int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                    int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
+                    float scale, uint16_t* out, void* stream) {
+  if (!A || !B || !out) return QLORA_ERR_INVALID_ARG;
+  int st = check_store(codes, absmax_q, absmax_s2);
+  if (st != QLORA_OK) return st;
+  if (N <= 0 || K <= 0) return QLORA_ERR_INVALID_ARG;
+  if (K % QLORA_NF4_BLOCK != 0 || r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30 || (N + 63) / 64 > 65535)
+    return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(A, 2) || !aligned(B, 2) || !aligned(out, 16)) return QLORA_ERR_UNSUPPORTED;
+  return hip_status(qlora::launch_nf4_merge(codes, absmax_q, absmax_s2, N, K, A, B, r, scale,
+                                            out, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (check_linear_shape(M, N, K, r) != QLORA_OK) return 0;
   return qlora::linear_workspace_bytes(M, N, K, r);

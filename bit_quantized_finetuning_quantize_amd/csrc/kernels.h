@@ -23,6 +23,12 @@ hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
                                  const float* absmax_s2, int64_t numel, void* out,
                                  bool bf16, hipStream_t stream);
 
+// Merged 16-bit weight: bf16(w' + s (A B)^T), [N x K] row-major.
+hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q,
+                            const float* absmax_s2, int64_t N, int64_t K, const uint16_t* A,
+                            const uint16_t* B, int r, float scale, uint16_t* out,
+                            hipStream_t stream);
+
 // ---- linear layer -----------------------------------------------------------
 
 // Workspace carve-up for the forward and backward of one linear call.

@@ -211,6 +211,93 @@ hipError_t launch_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
   return hipGetLastError();
 }
 
+// Adapter merge (ozercemkelahmet.com "QLoRA", How it works, Step 8: save
+// and use, the option that dequantizes the base to 16 bits and merges the
+// adapter; same page, "Merging after QLoRA"):
+//   out[n][k] = bf16( w'[n][k] + s * sum_j A[k][j] B[j][n] )
+// with the sum in float32 from j = 0 upward (each product of two bf16
+// values is exact, so one fma per term rounds exactly like an add), then
+// fl32(s * sum), fl32(w' + that) and one round-to-nearest-even to bf16.
+// Workgroup: 64 weight rows x 64 columns (one block per row); thread: two
+// rows x eight columns (one code dword per row). The adapter is staged in
+// LDS as float32 in chunks of 32 ranks: A transposed ([j][k]) and B as is
+// ([j][n]).
+constexpr int kMergeRC = 32;
+__global__ void __launch_bounds__(256)
+nf4_merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
+                 const float* __restrict__ absmax_s2, int64_t N, int64_t K,
+                 const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r,
+                 float s, uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
+  __shared__ float s_lv[16];
+  __shared__ __attribute__((aligned(16))) float s_at[kMergeRC][64];  // A[k0 + k][j0 + j]
+  __shared__ __attribute__((aligned(16))) float s_b[kMergeRC][64];   // B[j0 + j][n0 + n]
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int rp = tid >> 3, cr = tid & 7;
+  const int64_t k = k0 + 8 * cr;
+  if (tid < 16) s_lv[tid] = kNF4[tid];
+
+  float acc[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+
+  for (int j0 = 0; j0 < r; j0 += kMergeRC) {
+    const int jn = min(kMergeRC, r - j0);
+    __syncthreads();  // the previous chunk is consumed
+    for (int i = tid; i < kMergeRC * 64; i += 256) {
+      const int j = i >> 6, c = i & 63;
+      const int64_t kk = k0 + c, nn = n0 + c;
+      s_at[j][c] = (j < jn) ? bf16_to_f32(A[kk * r + j0 + j]) : 0.0f;
+      s_b[j][c] = (j < jn && nn < N) ? bf16_to_f32(B[(int64_t)(j0 + j) * N + nn]) : 0.0f;
+    }
+    __syncthreads();
+    for (int j = 0; j < jn; ++j) {
+      const floatx4 a0 = *reinterpret_cast<const floatx4*>(&s_at[j][8 * cr]);
+      const floatx4 a1 = *reinterpret_cast<const floatx4*>(&s_at[j][8 * cr + 4]);
+      const float b0 = s_b[j][2 * rp], b1 = s_b[j][2 * rp + 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[0][e] = __builtin_fmaf(a0[e], b0, acc[0][e]);
+        acc[0][e + 4] = __builtin_fmaf(a1[e], b0, acc[0][e + 4]);
+        acc[1][e] = __builtin_fmaf(a0[e], b1, acc[1][e]);
+        acc[1][e + 4] = __builtin_fmaf(a1[e], b1, acc[1][e + 4]);
+      }
+    }
+  }
+  __syncthreads();  // s_lv (written before the rank loop) is visible
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t n = n0 + 2 * rp + h;
+    if (n >= N) continue;
+    const int64_t e0 = n * K + k;                       // first of 8 elements, one block
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
+    const int64_t b = e0 / kBlock;
+    const float cs = block_scale(absmax_q[b], absmax_s2[b / kGroup]);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float w0 = s_lv[(word >> (4 * e)) & 15u] * cs;
+      const float w1 = s_lv[(word >> (4 * e + 4)) & 15u] * cs;
+      const float t0 = s * acc[h][e], t1 = s * acc[h][e + 1];
+      o[e / 2] = pack_bf16x2(w0 + t0, w1 + t1);
+    }
+    *reinterpret_cast<u32x4*>(out + e0) = o;
+  }
+}
+
+hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q,
+                            const float* absmax_s2, int64_t N, int64_t K, const uint16_t* A,
+                            const uint16_t* B, int r, float scale, uint16_t* out,
+                            hipStream_t stream) {
+  dim3 grid((unsigned)(K / 64), (unsigned)((N + 63) / 64));
+  hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), 0, stream, codes, absmax_q, absmax_s2, N,
+                     K, A, B, r, scale, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
                                  const float* absmax_s2, int64_t numel, void* out,
                                  bool bf16, hipStream_t stream) {

@@ -129,6 +129,26 @@ int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
                               const float* absmax_s2, int64_t numel,
                               uint16_t* out, void* stream);
 
+/* qlora_nf4_merge — the adapter folded into a 16-bit copy of the frozen
+ * weight (ozercemkelahmet.com "QLoRA", How it works, Step 8: save and use:
+ * dequantize the base to 16 bits and merge the adapter; same page, "Merging
+ * after QLoRA"). With A [K x r] and B [r x N] as in the linear calls, a
+ * forward pass computes X (W' + s (A B)^T)^T, so
+ *   out[n][k] = bf16( w'[n][k] + scale * sum_j A[k][j] B[j][n] )
+ * in this order: the sum in float32 from j = 0 upward (each product of two
+ * bf16 values is exact), then fl32(scale * sum), fl32(w' + that), one
+ * round-to-nearest-even to bf16. Deterministic.
+ *   codes, absmax_q, absmax_s2   the store of W [N x K] (numel = N*K)
+ *   A        device bf16 [K x r];  B  device bf16 [r x N]   (2-byte aligned)
+ *   out      device bf16 [N x K], 16-byte aligned, written
+ * Errors: INVALID_ARG for a null pointer or N, K <= 0; UNSUPPORTED if K is
+ * not a multiple of 64, r is outside [1, 256], N or K exceeds 2^30 (or N
+ * needs more than 65535 row tiles of 64), `codes` is not 16-byte aligned,
+ * `absmax_s2` not 4-byte aligned or `out` not 16-byte aligned. */
+int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                    int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
+                    float scale, uint16_t* out, void* stream);
+
 /* ---- the linear layer ------------------------------------------------------
  * Shapes: X [M x K], frozen weight W [N x K] in the NF4 store (numel = N*K,
  * blocks run along K), A [K x r], B [r x N], Y and dY [M x N].

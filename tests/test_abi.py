@@ -120,3 +120,21 @@ def test_workspace_query(lib):
     assert lib.qlora_linear_workspace_bytes(16, 4096, 4096, 16) > 0
     assert lib.qlora_linear_workspace_bytes(2048, 11008, 4096, 64) > 0
     assert lib.qlora_linear_workspace_bytes(16, 4096, 4000, 16) == 0
+
+
+def _merge(lib, N=128, K=128, r=8, codes=FAKE, A=FAKE, out=FAKE, s2=FAKE):
+    return lib.qlora_nf4_merge(codes, FAKE, s2, N, K, A, FAKE, r, 0.25, out, None)
+
+
+def test_merge_rejects(lib):
+    assert _merge(lib, codes=None) == -1
+    assert _merge(lib, A=None) == -1
+    assert _merge(lib, out=None) == -1
+    assert _merge(lib, N=0) == -1
+    assert _merge(lib, K=-64) == -1
+    assert _merge(lib, K=100) == -2        # K % 64
+    assert _merge(lib, r=0) == -2
+    assert _merge(lib, r=257) == -2
+    assert _merge(lib, out=ODD) == -2
+    assert _merge(lib, codes=ODD) == -2
+    assert _merge(lib, N=65536 * 64 + 1) == -2   # more than 65535 row tiles
