@@ -295,6 +295,22 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     qb.record()
     torch.cuda.synchronize()
     mms = qa.elapsed_time(qb) / 10
+    # AdamW step over every adapter of the 32-layer 7B-style stack at r = 64
+    na = 32 * r * (4 * (4096 + 4096) + 2 * (4096 + 11008) + (11008 + 4096))
+    st_p, st_m, st_v, st_g = (torch.zeros(na, dtype=torch.float32, device=dev) for _ in range(4))
+    st_16 = torch.empty(na, dtype=torch.bfloat16, device=dev)
+    for t in range(1, 3):
+        q.qlora_adamw_step(st_p, st_m, st_v, st_g, 2e-4, step=t, weight_decay=0.01, p_bf16=st_16)
+    torch.cuda.synchronize()
+    qa.record()
+    for t in range(3, 8):
+        q.qlora_adamw_step(st_p, st_m, st_v, st_g, 2e-4, step=t, weight_decay=0.01, p_bf16=st_16)
+    qb.record()
+    torch.cuda.synchronize()
+    ams = qa.elapsed_time(qb) / 5
+    res["adamw"] = dict(params=na, ms=ams, bytes_per_param=30,
+                        GBps=30 * na / (ams * 1e-3) / 1e9)
+    del st_p, st_m, st_v, st_g, st_16
     res["merge"] = dict(shape=[11008, 4096], rank=r, ms=mms,
                         GBps=(st0.nbytes() + 2 * W0.numel()) / (mms * 1e-3) / 1e9,
                         rank_flops_TFLOPs=2 * W0.numel() * r / (mms * 1e-3) / 1e12)
@@ -486,6 +502,7 @@ def main():
         },
         "quantize": pre["quantize"],
         "merge": pre["merge"],
+        "adamw": pre["adamw"],
         "gemv": gemv,
         "cpu_baseline": cpu,
     }

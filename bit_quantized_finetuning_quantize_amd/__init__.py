@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     Nf4Store,
     QloraError,
     empty_store,
+    qlora_adamw_step,
     qlora_linear_bwd,
     qlora_linear_fwd,
     qlora_linear_workspace_bytes,

@@ -113,6 +113,21 @@ def qlora_nf4_merge(st, A, B, scale, out=None):
     return out
 
 
+def qlora_adamw_step(p, m, v, g, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                     step=1, p_bf16=None):
+    """One AdamW step in place on float32 p, m, v with gradient g (same
+    number of elements); writes bf16(p) into p_bf16 when given."""
+    n = p.numel()
+    for t in (m, v, g):
+        if t.numel() != n or t.dtype != torch.float32:
+            raise QloraError("p, m, v, g must be float32 tensors of one size")
+    if p_bf16 is not None and p_bf16.numel() != n:
+        raise QloraError("p_bf16 must have as many elements as p")
+    _check(LIB.qlora_adamw_step(_ptr(p), _ptr(m), _ptr(v), _ptr(g), n, float(lr), float(beta1),
+                                float(beta2), float(eps), float(weight_decay), int(step),
+                                _ptr(p_bf16) if p_bf16 is not None else None, _stream()))
+
+
 def qlora_linear_workspace_bytes(M, N, K, r):
     return int(LIB.qlora_linear_workspace_bytes(M, N, K, r))
 

@@ -29,6 +29,12 @@ hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q,
                             const uint16_t* B, int r, float scale, uint16_t* out,
                             hipStream_t stream);
 
+// One AdamW step over n float32 parameters with float32 moments (in place);
+// p16 (optional) receives bf16(p).
+hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n, float lr,
+                        float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                        uint16_t* p16, hipStream_t stream);
+
 // ---- linear layer -----------------------------------------------------------
 
 // Workspace carve-up for the forward and backward of one linear call.

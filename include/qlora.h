@@ -149,6 +149,28 @@ int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* 
                     int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
                     float scale, uint16_t* out, void* stream);
 
+/* qlora_adamw_step — one AdamW step for adapter parameters, in place
+ * (ozercemkelahmet.com "QLoRA", "Practical guidance and best practices",
+ * Optimizer and schedule: a paged 8-bit or 32-bit AdamW; same page, "How it
+ * works", Step 7). Float32 parameters p, moments m and v, gradient g (for
+ * example dA or dB of qlora_linear_bwd), n elements each; step t >= 1 counts
+ * from 1. Each operation is one float32 operation rounded on its own, in
+ * this order (host constants computed in float64 and rounded once):
+ *   lw = lr*wd, c1 = 1 - beta1^t, c2 = 1 - beta2^t
+ *   p1 = p - lw*p
+ *   m  = beta1*m + (1-beta1)*g
+ *   v  = beta2*v + (1-beta2)*(g*g)
+ *   p  = p1 - lr*((m/c1) / (sqrt(v/c2) + eps))
+ * p_bf16 (optional, device uint16 [n]) receives bf16(p), the copy that the
+ * linear calls take as A or B. The state may be device memory or managed
+ * memory that pages to the host; the call only streams through it.
+ * Errors: INVALID_ARG for a null pointer, n <= 0, step < 1, beta outside
+ * [0, 1) or eps <= 0; UNSUPPORTED for float arrays not 4-byte aligned or
+ * p_bf16 not 2-byte aligned. */
+int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, float lr,
+                     float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                     uint16_t* p_bf16, void* stream);
+
 /* ---- the linear layer ------------------------------------------------------
  * Shapes: X [M x K], frozen weight W [N x K] in the NF4 store (numel = N*K,
  * blocks run along K), A [K x r], B [r x N], Y and dY [M x N].

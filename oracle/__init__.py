@@ -38,3 +38,4 @@ from .nf4 import (  # noqa: F401
 from .bf16 import bf16_round, bf16_bits_to_f32, f32_to_bf16_bits  # noqa: F401
 from .linear import linear_fwd, linear_bwd  # noqa: F401
 from .merge import merge  # noqa: F401
+from .adamw import adamw_step  # noqa: F401

@@ -138,3 +138,20 @@ def test_merge_rejects(lib):
     assert _merge(lib, out=ODD) == -2
     assert _merge(lib, codes=ODD) == -2
     assert _merge(lib, N=65536 * 64 + 1) == -2   # more than 65535 row tiles
+
+
+def test_adamw_rejects(lib):
+    a = lib.qlora_adamw_step
+    ok = [FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None, None]
+    bad = list(ok); bad[0] = None
+    assert a(*bad) == -1
+    bad = list(ok); bad[4] = 0
+    assert a(*bad) == -1
+    bad = list(ok); bad[10] = 0      # step counts from 1
+    assert a(*bad) == -1
+    bad = list(ok); bad[6] = 1.0     # beta1 outside [0, 1)
+    assert a(*bad) == -1
+    bad = list(ok); bad[8] = 0.0     # eps
+    assert a(*bad) == -1
+    bad = list(ok); bad[1] = ODD
+    assert a(*bad) == -2
