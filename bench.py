@@ -283,6 +283,24 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     qms = qa.elapsed_time(qb) / 10
     res["quantize"] = dict(shape=[11008, 4096], ms=qms,
                            GBps=(2 * W0.numel() + st0.nbytes()) / (qms * 1e-3) / 1e9)
+    # standalone dequantization of the same store, float32 and bf16 out
+    w32 = torch.empty(W0.numel(), dtype=torch.float32, device=dev)
+    w16 = torch.empty(W0.numel(), dtype=torch.bfloat16, device=dev)
+    deq = {}
+    for name, fn, outb, bpe in (("f32", q.qlora_nf4_dequantize, w32, 4),
+                                ("bf16", q.qlora_nf4_dequantize_bf16, w16, 2)):
+        for _ in range(3):
+            fn(st0, out=outb)
+        torch.cuda.synchronize()
+        qa.record()
+        for _ in range(10):
+            fn(st0, out=outb)
+        qb.record()
+        torch.cuda.synchronize()
+        dms = qa.elapsed_time(qb) / 10
+        deq[name] = dict(ms=dms, GBps=(st0.nbytes() + bpe * W0.numel()) / (dms * 1e-3) / 1e9)
+    res["dequantize"] = dict(shape=[11008, 4096], **deq)
+    del w32, w16
     # adapter merge into a bf16 copy of the same weight (store in, bf16 out)
     A0, B0 = projs[0]["A"], projs[0]["B"]
     merged = q.qlora_nf4_merge(st0, A0, B0, s)
@@ -501,6 +519,7 @@ def main():
             "avg_launch_ms": round(pre["dx_kernel_ms"], 4),
         },
         "quantize": pre["quantize"],
+        "dequantize": pre["dequantize"],
         "merge": pre["merge"],
         "adamw": pre["adamw"],
         "gemv": gemv,

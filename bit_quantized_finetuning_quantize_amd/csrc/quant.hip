@@ -114,13 +114,31 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
     const int64_t e0 = gbase + (int64_t)r * (kQuantThreads * 8) + tid * 8;
     if (e0 >= numel) continue;
     const float c = cmax[r];
+    // n = w / c. For c in [2^-100, 2^100] the product with v_rcp_f32(c) gives
+    // the same NF4 index as the correctly rounded quotient for every bf16
+    // pair |w| <= c (checked exhaustively on gfx950: 1,065,402,238 pairs, no
+    // difference inside that range, differences only beyond it, where the
+    // reciprocal leaves the normal range); outside it the IEEE division.
+    float n[8];
+    if (c >= 0x1p-100f && c <= 0x1p100f) {
+      const float rc = __builtin_amdgcn_rcpf(c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        n[2 * i] = bf16_lo(vals[r][i]) * rc;
+        n[2 * i + 1] = bf16_hi(vals[r][i]) * rc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        n[2 * i] = bf16_lo(vals[r][i]) / c;   // IEEE division
+        n[2 * i + 1] = bf16_hi(vals[r][i]) / c;
+      }
+    }
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = bf16_lo(vals[r][i]);
-      const float b = bf16_hi(vals[r][i]);
-      uint32_t qa = (c > 0.0f) ? nf4_index(a / c, s_thr) : 7u;
-      uint32_t qb = (c > 0.0f) ? nf4_index(b / c, s_thr) : 7u;
+      uint32_t qa = (c > 0.0f) ? nf4_index(n[2 * i], s_thr) : 7u;
+      uint32_t qb = (c > 0.0f) ? nf4_index(n[2 * i + 1], s_thr) : 7u;
       // nibbles past the end of the tensor stay 0
       if (e0 + 2 * i >= numel) qa = 0u;
       if (e0 + 2 * i + 1 >= numel) qb = 0u;

@@ -108,6 +108,37 @@ def test_every_bf16_value_in_range(q):
         _roundtrip(q, w, f"bf16 grid |w|<={cb}")
 
 
+def _grid_blocks(cs):
+    """Blocks whose absmax is c, filled with every bf16 value of [-c, c]."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    out = []
+    for c in cs:
+        cb = float(bf16_round(np.float32(c)))
+        sel = vals[np.isfinite(vals) & (np.abs(vals) <= cb)]
+        nb = -(-sel.size // 63)
+        blocks = np.zeros((nb, 64), np.float32)
+        blocks[:, 0] = cb
+        blocks[1::2, 0] = -cb
+        blocks[:, 1:] = np.concatenate([sel, np.zeros(nb * 63 - sel.size, np.float32)]).reshape(nb, 63)
+        out.append(blocks.ravel())
+    return np.concatenate(out)
+
+
+def test_every_mantissa_pair(q):
+    """Every bf16 mantissa of the block constant c (c in [1, 2)) against every
+    bf16 value of [-c, c]: all (mantissa of w, mantissa of c, exponent gap)
+    combinations that the normalization w / c sees, so the codes are checked
+    for every quotient the division can produce away from float32's range
+    ends. Also c just inside and just outside [2^-100, 2^100], where the
+    kernel switches between its reciprocal product and the IEEE division."""
+    dev = device()
+    cs = [1.0 + m / 128.0 for m in range(128)]
+    cs += [2.0 ** -100, 2.0 ** -100 * (1 - 2 ** -8), 2.0 ** 100, 2.0 ** 100 * (1 + 2 ** -7)]
+    w = torch.from_numpy(_grid_blocks(cs)).to(torch.bfloat16).to(dev)
+    _roundtrip(q, w, "bf16 grid, every mantissa of c")
+
+
 def test_special_blocks(q):
     dev = device()
     rng = np.random.default_rng(0)
