@@ -39,3 +39,11 @@ from .bf16 import bf16_round, bf16_bits_to_f32, f32_to_bf16_bits  # noqa: F401
 from .linear import linear_fwd, linear_bwd  # noqa: F401
 from .merge import merge  # noqa: F401
 from .adamw import adamw_step  # noqa: F401
+from .philox import philox4x32_10  # noqa: F401
+from .dropout import (  # noqa: F401
+    dropout_keep,
+    keep_scale,
+    keep_threshold,
+    pack_keep,
+    unpack_keep,
+)
