@@ -332,6 +332,43 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     res["merge"] = dict(shape=[11008, 4096], rank=r, ms=mms,
                         GBps=(st0.nbytes() + 2 * W0.numel()) / (mms * 1e-3) / 1e9,
                         rank_flops_TFLOPs=2 * W0.numel() * r / (mms * 1e-3) / 1e12)
+    # the same step with LoRA dropout p = 0.05 on every adapter input: one
+    # keep mask drawn per projection and step, fwd and bwd through it
+    pd = 0.05
+    masks = [torch.empty(M, pr["K"] // 32, dtype=torch.int32, device=dev) for pr in projs]
+
+    def dstep(it):
+        for i, pr in enumerate(projs):
+            q.qlora_dropout_mask(M, pr["K"], pd, 1234 + i, it, out=masks[i])
+            q.qlora_linear_fwd_dropout(pr["X"], pr["st"], pr["A"], pr["B"], s, masks[i], pd,
+                                       Y=pr["Y"], T=pr["T"], ws=ws)
+            q.qlora_linear_bwd_dropout(pr["dY"], pr["X"], pr["T"], pr["st"], pr["A"], pr["B"], s,
+                                       masks[i], pd, dX=pr["dX"], dA=pr["dA"], dB=pr["dB"],
+                                       ws=ws)
+
+    for it in range(args.warmup):
+        dstep(it)
+    torch.cuda.synchronize()
+    qa.record()
+    for it in range(args.steps):
+        dstep(args.warmup + it)
+    qb.record()
+    torch.cuda.synchronize()
+    dms = qa.elapsed_time(qb) / args.steps
+    mk = masks[2]  # the down projection's input, 2048 x 11008
+    for _ in range(2):
+        q.qlora_dropout_mask(M, 11008, pd, 1, 0, out=mk)
+    torch.cuda.synchronize()
+    qa.record()
+    for it in range(10):
+        q.qlora_dropout_mask(M, 11008, pd, 1, it, out=mk)
+    qb.record()
+    torch.cuda.synchronize()
+    mkms = qa.elapsed_time(qb) / 10
+    res["dropout"] = dict(p=pd, ms_per_step=dms, tflops=flops_step / (dms * 1e-3) / 1e12,
+                          mask_shape=[M, 11008], mask_ms=mkms,
+                          mask_Gelem_per_s=M * 11008 / (mkms * 1e-3) / 1e9)
+    del masks
     return res, projs
 
 
@@ -522,6 +559,7 @@ def main():
         "dequantize": pre["dequantize"],
         "merge": pre["merge"],
         "adamw": pre["adamw"],
+        "dropout": pre["dropout"],
         "gemv": gemv,
         "cpu_baseline": cpu,
     }

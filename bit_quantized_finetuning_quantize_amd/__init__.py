@@ -8,8 +8,11 @@ from .api import (  # noqa: F401
     QloraError,
     empty_store,
     qlora_adamw_step,
+    qlora_dropout_mask,
     qlora_linear_bwd,
+    qlora_linear_bwd_dropout,
     qlora_linear_fwd,
+    qlora_linear_fwd_dropout,
     qlora_linear_workspace_bytes,
     qlora_nf4_codebook,
     qlora_nf4_codes_bytes,

@@ -32,6 +32,14 @@ SIGNATURES = {
     "qlora_nf4_merge": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i32, _c_f32, _vp,
                                  _vp]),
     "qlora_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i32]),
+    "qlora_dropout_mask": (_c_int, [_c_i64, _c_i64, _c_f32, ctypes.c_uint64, ctypes.c_uint64, _vp,
+                                    _vp]),
+    "qlora_linear_fwd_dropout": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                          _c_i32, _c_f32, _vp, _c_f32, _vp, _vp, _vp, _c_size,
+                                          _vp]),
+    "qlora_linear_bwd_dropout": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
+                                          _c_i64, _c_i32, _c_f32, _vp, _c_f32, _vp, _vp, _vp, _vp,
+                                          _c_size, _vp]),
     "qlora_linear_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32,
                                   _c_f32, _vp, _vp, _vp, _c_size, _vp]),
     "qlora_linear_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,

@@ -184,3 +184,60 @@ def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, d
                                          _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(),
                                          ev[0], ev[1]))
     return (dX if want_dX else None), dA, dB
+
+
+def qlora_dropout_mask(M, K, p, seed, offset=0, out=None, device=None):
+    """Keep mask of LoRA dropout over an [M x K] adapter input: int32 tensor
+    [M, K // 32] holding the uint32 bit words (bit j of word w of row m keeps
+    element (m, 32 w + j))."""
+    if out is None:
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        out = torch.empty(M, K // 32, dtype=torch.int32, device=dev)
+    _need(out, torch.int32, "mask")
+    _check(LIB.qlora_dropout_mask(M, K, float(p), int(seed) & (2**64 - 1),
+                                  int(offset) & (2**64 - 1), _ptr(out), _stream()))
+    return out
+
+
+def qlora_linear_fwd_dropout(X, W, A, B, scale, keep_mask, p, want_T=True, Y=None, T=None,
+                             ws=None):
+    """qlora_linear_fwd with LoRA dropout on the adapter input; returns
+    (Y, T) with T = D(X) A (fp32) or None."""
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[1]
+    for t, name in ((X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, name)
+    _need(keep_mask, torch.int32, "keep_mask")
+    Y = Y if Y is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    if want_T and T is None:
+        T = torch.empty(M, r, dtype=torch.float32, device=X.device)
+    ws = ws if ws is not None else workspace(M, N, K, r, X.device)
+    _check(LIB.qlora_linear_fwd_dropout(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q),
+                                        _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r,
+                                        float(scale), _ptr(keep_mask), float(p), _ptr(Y),
+                                        _ptr(T) if want_T else None, _ptr(ws), ws.numel(),
+                                        _stream()))
+    return Y, (T if want_T else None)
+
+
+def qlora_linear_bwd_dropout(dY, X, T, W, A, B, scale, keep_mask, p, want_dX=True, dX=None,
+                             dA=None, dB=None, ws=None):
+    """qlora_linear_bwd with LoRA dropout; returns (dX or None, dA, dB)."""
+    M, N = dY.shape
+    K = X.shape[1]
+    r = A.shape[1]
+    for t, name in ((dY, "dY"), (X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, name)
+    _need(keep_mask, torch.int32, "keep_mask")
+    if want_dX and dX is None:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    dA = dA if dA is not None else torch.empty(K, r, dtype=torch.float32, device=X.device)
+    dB = dB if dB is not None else torch.empty(r, N, dtype=torch.float32, device=X.device)
+    ws = ws if ws is not None else workspace(M, N, K, r, X.device)
+    _check(LIB.qlora_linear_bwd_dropout(_ptr(dY), _ptr(X), _ptr(T), _ptr(W.codes),
+                                        _ptr(W.absmax_q), _ptr(W.absmax_s2), _ptr(A), _ptr(B),
+                                        M, N, K, r, float(scale), _ptr(keep_mask), float(p),
+                                        _ptr(dX) if want_dX else None, _ptr(dA), _ptr(dB),
+                                        _ptr(ws), ws.numel(), _stream()))
+    return (dX if want_dX else None), dA, dB

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlora.so")
-SOURCES = ["quant.hip", "gemv.hip", "linear.hip", "adamw.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemv.hip", "linear.hip", "adamw.hip", "dropout.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

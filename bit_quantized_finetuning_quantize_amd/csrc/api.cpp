@@ -3,6 +3,7 @@
 // effects and makes no HIP call.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -35,6 +36,25 @@ int check_linear_shape(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (K % QLORA_NF4_BLOCK != 0 || N % QLORA_NF4_BLOCK != 0) return QLORA_ERR_UNSUPPORTED;
   if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return QLORA_ERR_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+// 16-bit keep threshold of a drop probability p in [0, 1): floor(p 2^16 + 1/2)
+// (p * 2^16 is exact in double). Returns -1 for p outside [0, 1) or NaN, and
+// 65536 when p rounds to certain dropping.
+int64_t keep_threshold(float p) {
+  if (!(p >= 0.0f && p < 1.0f)) return -1;
+  return (int64_t)std::floor((double)p * 65536.0 + 0.5);
+}
+
+int check_dropout(const uint32_t* mask, float p, qlora::Dropout* dr) {
+  if (!mask) return QLORA_ERR_INVALID_ARG;
+  const int64_t thr = keep_threshold(p);
+  if (thr < 0) return QLORA_ERR_INVALID_ARG;
+  if (thr >= 65536) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(mask, 4)) return QLORA_ERR_UNSUPPORTED;
+  dr->mask = mask;
+  dr->keep_scale = (float)(65536.0 / (double)(65536 - thr));
   return QLORA_OK;
 }
 
@@ -182,6 +202,70 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, cons
                      void* stream) {
   return qlora_linear_bwd_profiled(dY, X, T, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale,
                                    dX, dA, dB, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+int qlora_dropout_mask(int64_t M, int64_t K, float p, uint64_t seed, uint64_t offset,
+                       uint32_t* mask, void* stream) {
+  if (!mask || M <= 0 || K <= 0) return QLORA_ERR_INVALID_ARG;
+  const int64_t thr = keep_threshold(p);
+  if (thr < 0) return QLORA_ERR_INVALID_ARG;
+  if (thr >= 65536 || K % 32 != 0 || !aligned(mask, 4)) return QLORA_ERR_UNSUPPORTED;
+  if (M > ((int64_t)1 << 40) / K) return QLORA_ERR_UNSUPPORTED;
+  return hip_status(qlora::launch_dropout_mask(M, K, (uint32_t)thr, seed, offset, mask,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qlora_linear_fwd_dropout(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                             const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                             int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                             const uint32_t* keep_mask, float p, uint16_t* Y, float* T_out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  int st = check_store(codes, absmax_q, absmax_s2);
+  if (st != QLORA_OK) return st;
+  st = check_linear_shape(M, N, K, r);
+  if (st != QLORA_OK) return st;
+  qlora::Dropout dr;
+  st = check_dropout(keep_mask, p, &dr);
+  if (st != QLORA_OK) return st;
+  if (!aligned(X, 16) || !aligned(B, 16) || !aligned(A, 2) || !aligned(Y, 2) ||
+      (T_out && !aligned(T_out, 4)))
+    return QLORA_ERR_UNSUPPORTED;
+  const size_t need = qlora::linear_workspace_bytes(M, N, K, r);
+  if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  // every M takes the MFMA path: the keep mask enters the X A contraction
+  return hip_status(qlora::launch_fwd_gemm(X, W, A, B, M, N, K, r, scale, Y, T_out, ws,
+                                           reinterpret_cast<hipStream_t>(stream), nullptr,
+                                           nullptr, dr));
+}
+
+int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* X, const float* T,
+                             const uint8_t* codes, const uint8_t* absmax_q,
+                             const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                             int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                             const uint32_t* keep_mask, float p, uint16_t* dX, float* dA,
+                             float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (!dY || !X || !A || !B || !dA || !dB) return QLORA_ERR_INVALID_ARG;
+  int st = check_store(codes, absmax_q, absmax_s2);
+  if (st != QLORA_OK) return st;
+  st = check_linear_shape(M, N, K, r);
+  if (st != QLORA_OK) return st;
+  qlora::Dropout dr;
+  st = check_dropout(keep_mask, p, &dr);
+  if (st != QLORA_OK) return st;
+  if (dX && r > QLORA_MAX_DROPOUT_RANK) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(B, 16) || !aligned(A, 2) ||
+      (T && !aligned(T, 4)) || (dX && !aligned(dX, 2)) || !aligned(dA, 4) || !aligned(dB, 4))
+    return QLORA_ERR_UNSUPPORTED;
+  const size_t need = qlora::linear_workspace_bytes(M, N, K, r);
+  if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  return hip_status(qlora::launch_bwd(dY, X, T, W, A, B, M, N, K, r, scale, dX, dA, dB, ws,
+                                      reinterpret_cast<hipStream_t>(stream), nullptr, nullptr,
+                                      dr));
 }
 
 const char* qlora_status_string(int status) {

@@ -138,32 +138,117 @@ struct DirectRows {
   __device__ __forceinline__ void store(const Regs&, uint32_t, const Tables&, int) const {}
 };
 
+// LoRA dropout keep bits (row-major [rows][ld] words, bit j of word w is
+// column 32 w + j) as AND masks over eight bf16 values: bit i of `bits`
+// keeps element i, i.e. half (i & 1) of word i / 2.
+__device__ __forceinline__ u32x4 keep_mask8(uint32_t bits) {
+  u32x4 m;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = 0u - ((bits >> (2 * w)) & 1u);
+    const uint32_t hi = 0u - ((bits >> (2 * w + 1)) & 1u);
+    m[w] = (lo & 0xffffu) | (hi & 0xffff0000u);
+  }
+  return m;
+}
+
+// Rows of a row-major bf16 matrix with a dropout keep mask applied on the
+// way into LDS (dropped elements become +0): through registers, one unit is
+// 16 contraction elements of one row. Rows at or past `rows` read as zero.
+template <int R>
+struct MaskedRows {
+  static constexpr bool kWideConsumers = false;
+  static constexpr int kUnits = R * 4;
+  static constexpr int kPer = (kUnits + kProducerThreads - 1) / kProducerThreads;
+  static constexpr int kDirect = 0;
+  static constexpr int kRegLoads = 3 * kPer;
+  const uint16_t* base;
+  int64_t ld;    // elements between rows
+  int64_t rows;  // valid rows
+  const uint32_t* mask;  // keep bits, [rows][mld] words
+  int64_t mld;
+  const void* rb; int64_t rn; const void* mb; int64_t mn;
+  int voff[kPer], moff[kPer];
+  struct Regs { u32x4 x[kPer][2]; uint32_t m[kPer]; };
+  __device__ __forceinline__ void setup(int64_t row0, int t) {
+    rb = base + row0 * ld;
+    rn = (rows - row0) * ld * 2;
+    mb = mask + row0 * mld;
+    mn = (rows - row0) * mld * 4;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int id = t + u * kProducerThreads;
+      const int row = id >> 2, q = id & 3;
+      const bool ok = id < kUnits;
+      voff[u] = ok ? (int)(row * ld * 2) + q * 32 : 0x7ffffff0;
+      moff[u] = ok ? (int)(row * mld * 4) + (q >> 1) * 4 : 0x7ffffff0;
+    }
+  }
+  __device__ __forceinline__ void direct(int, uint32_t, int) const {}
+  __device__ __forceinline__ void load(int step, Regs& r, int) const {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rb, rn);
+    const __amdgpu_buffer_rsrc_t msrc = make_rsrc(mb, mn);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        r.x[u][c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[u] + c * 16, step * (kStep * 2), 0));
+      r.m[u] = __builtin_amdgcn_raw_buffer_load_b32(msrc, moff[u], step * (kStep / 8), 0);
+    }
+  }
+  __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables&, int t) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int id = t + u * kProducerThreads;
+      if (id >= kUnits) continue;
+      const int row = id >> 2, q = id & 3;
+      const uint32_t bits = r.m[u] >> ((q & 1) * 16);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        *(lds_u32x4*)(uintptr_t)(tile + (uint32_t)tile_off(row, 2 * q + c)) =
+            r.x[u][c] & keep_mask8(bits >> (8 * c));
+    }
+  }
+};
+
 // Transposed bf16 source through registers: tile row i = source column
 // col0 + i, contraction = source row. Each unit is 4 source rows x 8 source
-// columns. Source rows at or past `rows` read as zero.
-template <int R>
+// columns. Source rows at or past `rows` read as zero. With kMask, a
+// dropout keep mask over the source ([rows][mld] words) zeroes the dropped
+// elements; a null mask keeps everything.
+template <int R, bool kMask = false>
 struct ColsBf16 {
   static constexpr bool kWideConsumers = false;
   static constexpr int kUnits = R * 2;
   static constexpr int kPer = (kUnits + kProducerThreads - 1) / kProducerThreads;
   static constexpr int kDirect = 0;
-  static constexpr int kRegLoads = 4 * kPer;
+  static constexpr int kRegLoads = (kMask ? 8 : 4) * kPer;
   const uint16_t* base;
   int64_t ld;    // elements between source rows
   int64_t rows;  // valid source rows (contraction length)
   int64_t cols;  // valid source columns
-  const void* rb; int64_t rn;
-  int voff[kPer];
-  struct Regs { u32x4 v[kPer][4]; };
+  const uint32_t* mask;  // kMask only: keep bits of the source, or null
+  int64_t mld;
+  const void* rb; int64_t rn; const void* mb; int64_t mn;
+  uint32_t mor;  // all ones when there is no mask
+  int voff[kPer], moff[kPer];
+  struct Regs { u32x4 v[kPer][4]; uint32_t m[kMask ? kPer : 1][4]; };
   __device__ __forceinline__ void setup(int64_t col0, int t) {
     rb = base + col0;
     rn = rows * ld * 2 - col0 * 2;
+    if constexpr (kMask) {
+      mb = mask ? mask + (col0 >> 5) : nullptr;
+      mn = mask ? rows * mld * 4 - (col0 >> 5) * 4 : 0;
+      mor = mask ? 0u : 0xffffffffu;
+    }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int id = t + u * kProducerThreads;
       const int rg = id % (R / 8), cg = id / (R / 8);
       const bool ok = id < kUnits && col0 + rg * 8 < cols;
       voff[u] = ok ? (int)((cg * 4) * ld * 2 + rg * 16) : 0x7ffffff0;
+      if constexpr (kMask) moff[u] = ok ? (int)((cg * 4) * mld * 4 + (rg >> 2) * 4) : 0x7ffffff0;
     }
   }
   __device__ __forceinline__ void direct(int, uint32_t, int) const {}
@@ -176,13 +261,28 @@ struct ColsBf16 {
       for (int e = 0; e < 4; ++e)
         r.v[u][e] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[u] + (int)(e * ld * 2), soff, 0));
+    if constexpr (kMask) {
+      const int msoff = (int)((int64_t)step * kStep * mld * 4);
+      const __amdgpu_buffer_rsrc_t msrc = make_rsrc(mb, mn);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          r.m[u][e] = __builtin_amdgcn_raw_buffer_load_b32(msrc, moff[u] + (int)(e * mld * 4), msoff, 0);
+    }
   }
-  __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables&, int t) const {
+  __device__ __forceinline__ void store(const Regs& r_in, uint32_t tile, const Tables&, int t) const {
+    Regs r = r_in;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int id = t + u * kProducerThreads;
       if (id >= kUnits) continue;
       const int rg = id % (R / 8), cg = id / (R / 8);
+      if constexpr (kMask) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          r.v[u][e] &= keep_mask8(((r.m[u][e] | mor) >> ((rg & 3) * 8)) & 0xffu);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1, sh = (e & 1) * 16;
@@ -332,6 +432,7 @@ struct LoadNone {
 
 // bf16 output, row-major [P x Q] with leading dimension ld.
 struct EpiBf16 {
+  static constexpr bool kKeepSeg2 = false;
   uint16_t* out;
   int64_t ld, P, Q;
   __device__ __forceinline__ void put(int64_t p, int64_t q, float v) const {
@@ -339,8 +440,24 @@ struct EpiBf16 {
   }
 };
 
+// bf16 output whose second segment (the LoRA columns) passes through a
+// dropout keep mask over the output, [P][mld] words: C = seg1 + keep o seg2.
+// The consumers sum the second segment apart from the first and add only
+// its kept elements (at most three second-segment steps, one split).
+struct EpiBf16Keep {
+  static constexpr bool kKeepSeg2 = true;
+  uint16_t* out;
+  int64_t ld, P, Q;
+  const uint32_t* mask;
+  int64_t mld;
+  __device__ __forceinline__ void put(int64_t p, int64_t q, float v) const {
+    if (p < P && q < Q) out[p * ld + q] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+  }
+};
+
 // float32 split-K partial: out[split][p][q], dense [P x Q] per split.
 struct EpiPartial {
+  static constexpr bool kKeepSeg2 = false;
   float* out;
   int64_t P, Q;
   __device__ __forceinline__ void put(int64_t p, int64_t q, float v, int split) const {
@@ -410,6 +527,72 @@ struct Consumer {
     __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);      // MFMA kk = 1
     __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk = 3
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kM, 0);  // MFMA kk = 2, 3
+  }
+
+  // Keep bits of this lane's accumulator elements under a dropout mask over
+  // the output ([rows][mld] words; `mrs` covers the workgroup's rows, `qw`
+  // is the word column of the tile's first column): bit v of keep[i][j] is
+  // element v of block (i, j). A 64-bit load gives the words of both column
+  // blocks of a row. Read before the main loop, whose registers have room
+  // for the eight results.
+  template <int BPn = BP, int BQn = BQ>
+  __device__ __forceinline__ void load_keep(uint32_t (&keep)[BPn][BQn], __amdgpu_buffer_rsrc_t mrs,
+                                            int64_t mld, int qw, int wave, int lane) const {
+    static_assert(BQn == 2, "two 32-column blocks per wave: one 64-bit word pair per row");
+    const int wp = wave >> 1, wq = wave & 1;
+    const int wcol = (qw + (wq * WQ) / 32) * 4;
+#pragma unroll
+    for (int i = 0; i < BPn; ++i) {
+      keep[i][0] = 0u;
+      keep[i][1] = 0u;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int p = wp * WP + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const u32x2 w = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(mrs, (int)(p * mld * 4) + wcol, 0, 0));
+        keep[i][0] |= ((w[0] >> (lane & 31)) & 1u) << v;
+        keep[i][1] |= ((w[1] >> (lane & 31)) & 1u) << v;
+      }
+      // packed here, not after the main loop: the loaded words must not
+      // stay live across it
+      asm volatile("" : "+v"(keep[i][0]), "+v"(keep[i][1]));
+    }
+  }
+
+  // acc += keep o (sum over the LDS stages `st[0..ns)` of the tile product),
+  // one 32-row block at a time: the second segment's sum needs BQ extra
+  // accumulators, not BP * BQ.
+  __device__ __forceinline__ void add_kept(const uint32_t (&st)[3], int ns,
+                                           const uint32_t (&keep)[BP][BQ]) {
+#pragma unroll
+    for (int i = 0; i < BP; ++i) {
+      floatx16 lr[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) lr[j][v] = 0.0f;
+      for (int s = 0; s < ns; ++s) {
+        const uint32_t sA = st[s], sB = st[s] + (uint32_t)(PT * kRowBytes);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a = as_bf16x8(*(const lds_u32x4*)(uintptr_t)(sA + a_off[kk] + i * 32 * kRowBytes));
+#pragma unroll
+          for (int j = 0; j < BQ; ++j) {
+            const bf16x8 b = as_bf16x8(*(const lds_u32x4*)(uintptr_t)(sB + b_off[kk] + j * 32 * kRowBytes));
+            lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, lr[j], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          acc[i][j][v] += ((keep[i][j] >> v) & 1u) ? lr[j][v] : 0.0f;
+        // the sum is final here: the adds may not sink into the epilogue,
+        // which would keep every block's lr live at once
+        asm volatile("" : "+v"(acc[i][j]));
+      }
+    }
   }
 
   // Visit every accumulator element with its (p, q) tile coordinates.
@@ -508,7 +691,17 @@ __device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, 
         if (n1 > 1) a1.direct(g0 + 1, stage(1), tid);
       }
     }
-    for (int it = 0; it < n; ++it) {
+    // with a kept second segment the loop covers the first segment only;
+    // the second's stages are summed after the last barrier
+    const int nc = Epi::kKeepSeg2 ? n1 : n;
+    uint32_t keep[Epi::kKeepSeg2 ? Consumer<PT, QT, kCW>::BP : 1][2];
+    if constexpr (Epi::kKeepSeg2) {
+      const int64_t kp0 = (int64_t)pt * PT;
+      const __amdgpu_buffer_rsrc_t mrs =
+          make_rsrc(cfg.epi.mask + kp0 * cfg.epi.mld, (cfg.epi.P - kp0) * cfg.epi.mld * 4);
+      cons.load_keep(keep, mrs, cfg.epi.mld, (int)(((int64_t)qt * QT) >> 5), wave, lane);
+    }
+    for (int it = 0; it < nc; ++it) {
       if constexpr (kConsA) {
         // this wave's A loads of step it have landed (those of it+1 may fly)
         if (mover && it + 1 < n1) wait_vmcnt<LA1::kDirect>();
@@ -524,6 +717,13 @@ __device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, 
       cons.step(sA, sA + kBOff);
     }
     const int64_t p0 = (int64_t)pt * PT, q0 = (int64_t)qt * QT;
+    if constexpr (Epi::kKeepSeg2) {
+      for (int it = nc; it < n; ++it) stage_barrier();
+      // the second segment's stages (at most three) are all still in the
+      // ring: nothing is produced after the last barrier
+      const uint32_t st[3] = {stage(n1), stage(n1 + 1), stage(n1 + 2)};
+      cons.add_kept(st, min(n - n1, 3), keep);
+    }
     if constexpr (kPartial) {
       cons.for_each(wave, lane, [&](int p, int q, float v) { cfg.epi.put(p0 + p, q0 + q, v, split); });
     } else {

@@ -35,6 +35,21 @@ hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n,
                         float beta1, float beta2, float eps, float weight_decay, int64_t step,
                         uint16_t* p16, hipStream_t stream);
 
+// ---- LoRA dropout -------------------------------------------------------------
+
+// Keep mask of an [M x K] adapter input (K a multiple of 32): Philox4x32-10
+// with the 64-bit seed as key and (group, offset) as counter, one 16-bit
+// value per element compared with thr; bits packed [M][K/32].
+hipError_t launch_dropout_mask(int64_t M, int64_t K, uint32_t thr, uint64_t seed,
+                               uint64_t offset, uint32_t* mask, hipStream_t stream);
+
+// The mask and the inverse keep probability of one linear call; a null mask
+// means no dropout.
+struct Dropout {
+  const uint32_t* mask = nullptr;
+  float keep_scale = 1.0f;
+};
+
 // ---- linear layer -----------------------------------------------------------
 
 // Workspace carve-up for the forward and backward of one linear call.
@@ -54,7 +69,7 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int64_t M, int64_t N, int64_t K,
                            int r, float scale, uint16_t* Y, float* T_out, void* ws,
                            hipStream_t stream, hipEvent_t ev0 = nullptr,
-                           hipEvent_t ev1 = nullptr);
+                           hipEvent_t ev1 = nullptr, Dropout dr = Dropout{});
 
 // Backward: G = dY B^T, dX = [dY | s G] [W' ; A^T], dA = s X^T G, dB = s T^T dY.
 hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
@@ -62,7 +77,7 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
                       int64_t M, int64_t N, int64_t K, int r, float scale,
                       uint16_t* dX, float* dA, float* dB, void* ws,
                       hipStream_t stream, hipEvent_t ev0 = nullptr,
-                      hipEvent_t ev1 = nullptr);
+                      hipEvent_t ev1 = nullptr, Dropout dr = Dropout{});
 
 // Records `ev` on `stream` when it is not null (profiling hooks around the
 // dominant launch of a call).

@@ -20,6 +20,14 @@
 //   3. dX = dY W' + (sG) A^T   one contraction over N + r; the weight tile is
 //                         dequantized and transposed into LDS
 //   4. dA = X^T (sG),  dB = (sT)^T dY   split-M contractions -> reduce
+//
+// LoRA dropout (ozercemkelahmet.com "QLoRA", the LoraConfig of the code
+// section and "Practical guidance and best practices"): the adapter path
+// takes D(X) = (X o keep) f, f the inverse keep probability, from a keep
+// mask over X. The mask is applied where X enters the T and dA products
+// (on the way into LDS) and, for dX, to the LoRA columns' contribution,
+// summed apart from the frozen-weight product; f rides on the float32
+// reduction of T and G.
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -116,6 +124,20 @@ template __global__ void contraction_pair_kernel<128, 64, ColsBf16<128>, DirectR
     LoadNone, EpiPartial, true>(
     Contraction<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>,
     Contraction<128, 64, ColsBf16<128>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>, int);
+// with LoRA dropout
+template __global__ void contraction_kernel<256, 128, DirectRows<256>, Nf4Cols<128>,
+    DirectRows<256>, DirectRows<128>, EpiBf16Keep, false>(
+    Contraction<256, 128, DirectRows<256>, Nf4Cols<128>, DirectRows<256>, DirectRows<128>, EpiBf16Keep>);
+template __global__ void contraction_kernel<64, 64, MaskedRows<64>, DirectRows<64>, LoadNone,
+    LoadNone, EpiPartial, true>(
+    Contraction<64, 64, MaskedRows<64>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>);
+template __global__ void contraction_kernel<64, 64, MaskedRows<64>, ColsBf16<64>, LoadNone,
+    LoadNone, EpiPartial, true>(
+    Contraction<64, 64, MaskedRows<64>, ColsBf16<64>, LoadNone, LoadNone, EpiPartial>);
+template __global__ void contraction_pair_kernel<128, 64, ColsBf16<128, true>, DirectRows<64>,
+    LoadNone, LoadNone, EpiPartial, true>(
+    Contraction<128, 64, ColsBf16<128, true>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>,
+    Contraction<128, 64, ColsBf16<128, true>, DirectRows<64>, LoadNone, LoadNone, EpiPartial>, int);
 }  // namespace gemm
 
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
@@ -145,8 +167,10 @@ hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, 
                         hipStream_t stream);
 
 // Reduce split-K partials of an [M x r] low-rank product (partial layout
-// [split][M][ld]) and emit: float32 V (optional), bf16(s V) padded
-// [Mp x r64] (optional) and its transpose [r64 x Mp] (optional).
+// [split][M][ld]) and emit, with V = f * (sum of the partials): float32 V
+// (optional), bf16(s V) padded [Mp x r64] (optional) and its transpose
+// [r64 x Mp] (optional). f is the dropout keep scale (exactly 1 without
+// dropout, which leaves the sum unchanged).
 struct LowrankJob {
   const float* part;
   int splits;
@@ -154,6 +178,7 @@ struct LowrankJob {
   float* out32;
   uint16_t* sv;
   uint16_t* svt;
+  float f = 1.0f;
 };
 
 // One or two jobs of the same shape in one launch (the second one when
@@ -171,6 +196,7 @@ __global__ void reduce_lowrank_kernel(LowrankJob j0, LowrankJob j1, int64_t M, i
     float v = 0.0f;
     if (m < M && j < r) {
       for (int sp = 0; sp < jb.splits; ++sp) v += jb.part[((int64_t)sp * M + m) * jb.ld + j];
+      v *= jb.f;
       if (jb.out32) jb.out32[m * r + j] = v;
     }
     const uint16_t b = (uint16_t)(pack_bf16x2(s * v, 0.0f) & 0xffffu);
@@ -274,13 +300,13 @@ void set_steps(C& cfg, int64_t S1, int64_t S2, int64_t tiles) {
 }
 
 // Low-rank product V[M x r] = Aop[M x C] * Bop[r x C]^T with split-K partials.
-// Aop rows come from a bf16 row-major source (ld lda, contraction length C).
-template <class LB>
-hipError_t lowrank_partials(const uint16_t* a, int64_t lda, int64_t M, int64_t C, LB lb,
-                            int64_t r64, float* part, int* splits_out, hipStream_t stream) {
-  using LA = DirectRows<64>;
+// Aop rows come from a bf16 row-major source (DirectRows, or MaskedRows
+// under dropout), contraction length C.
+template <class LA, class LB>
+hipError_t lowrank_partials(LA la, int64_t M, int64_t C, LB lb, int64_t r64, float* part,
+                            int* splits_out, hipStream_t stream) {
   Contraction<64, 64, LA, LB, LoadNone, LoadNone, EpiPartial> cfg{};
-  cfg.a1 = LA{a, lda, M};
+  cfg.a1 = la;
   cfg.b1 = lb;
   cfg.nP = (int)ceil_div(M, 64);
   cfg.nQ = (int)(r64 / 64);
@@ -311,23 +337,34 @@ hipError_t prep_adapter(const uint16_t* A, int64_t K, int r, const WsLayout& w, 
   return hipGetLastError();
 }
 
-// T = X A -> out32 (optional), bf16(s T) [Mp x r64], bf16(s T)^T (optional).
-hipError_t compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
-                     const WsLayout& w, char* ws, float s, float* out32, bool transposed,
-                     hipStream_t stream) {
-  float* part = reinterpret_cast<float*>(ws + w.part);
-  int splits = 0;
+template <class LA>
+hipError_t T_partials(LA la, const uint16_t* A, int64_t M, int64_t K, int r, const WsLayout& w,
+                      char* ws, float* part, int* splits, hipStream_t stream) {
   if (adapter_in_place(A, r)) {
     // Bop[j][k] = A[k][j]: columns of the adapter, transposed on the way in
     ColsBf16<64> lb{A, (int64_t)r, K, (int64_t)r};
-    QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
-  } else {
-    // Bop[j][k] = A^T[j][k]: rows of the transposed, padded adapter copy
-    DirectRows<64> lb{reinterpret_cast<const uint16_t*>(ws + w.at), K, w.r64};
-    QLORA_TRY(lowrank_partials(X, K, M, K, lb, w.r64, part, &splits, stream));
+    return lowrank_partials(la, M, K, lb, w.r64, part, splits, stream);
   }
-  const LowrankJob jt{part, splits, w.r64, out32, reinterpret_cast<uint16_t*>(ws + w.st),
-                      transposed ? reinterpret_cast<uint16_t*>(ws + w.stt) : nullptr};
+  // Bop[j][k] = A^T[j][k]: rows of the transposed, padded adapter copy
+  DirectRows<64> lb{reinterpret_cast<const uint16_t*>(ws + w.at), K, w.r64};
+  return lowrank_partials(la, M, K, lb, w.r64, part, splits, stream);
+}
+
+// T = D(X) A -> out32 (optional), bf16(s T) [Mp x r64], bf16(s T)^T
+// (optional); D(X) = X without dropout (dr.mask null).
+hipError_t compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
+                     const WsLayout& w, char* ws, float s, float* out32, bool transposed,
+                     const Dropout& dr, hipStream_t stream) {
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  int splits = 0;
+  if (dr.mask)
+    QLORA_TRY(T_partials(MaskedRows<64>{X, K, M, dr.mask, K / 32}, A, M, K, r, w, ws, part,
+                         &splits, stream));
+  else
+    QLORA_TRY(T_partials(DirectRows<64>{X, K, M}, A, M, K, r, w, ws, part, &splits, stream));
+  LowrankJob jt{part, splits, w.r64, out32, reinterpret_cast<uint16_t*>(ws + w.st),
+                transposed ? reinterpret_cast<uint16_t*>(ws + w.stt) : nullptr};
+  if (dr.mask) jt.f = dr.keep_scale;
   hipLaunchKernelGGL(reduce_lowrank_kernel, dim3(grid_for(w.Mp * w.r64)), dim3(256), 0, stream,
                      jt, LowrankJob{}, M, r, w.r64, w.Mp, s);
   return hipGetLastError();
@@ -338,12 +375,12 @@ hipError_t compute_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K,
 hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int64_t M, int64_t N, int64_t K, int r,
                            float scale, uint16_t* Y, float* T_out, void* ws_,
-                           hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                           hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1, Dropout dr) {
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
   QLORA_TRY(prep_adapter(A, K, r, w, ws, stream));
   float* t32 = T_out ? T_out : reinterpret_cast<float*>(ws + w.t32);
-  QLORA_TRY(compute_T(X, A, M, K, r, w, ws, scale, t32, false, stream));
+  QLORA_TRY(compute_T(X, A, M, K, r, w, ws, scale, t32, false, dr, stream));
 
   using LA1 = DirectRows<256>;
   using LB1 = Nf4Rows<128>;
@@ -366,10 +403,76 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
   return record_if(ev1, stream);
 }
 
+namespace {
+
+// dX = dY W' + (second segment) on 256 x 128 tiles: the frozen weight's
+// tiles are dequantized and transposed into LDS, the LoRA columns
+// (s G | A^T) form the second segment.
+template <class Epi>
+hipError_t input_grad(const uint16_t* dY, Nf4Weight W, const uint16_t* apad, int64_t M,
+                      int64_t N, int64_t K, const WsLayout& w, char* ws, Epi epi,
+                      hipStream_t stream) {
+  using LA1 = DirectRows<256>;
+  using LB1 = Nf4Cols<128>;
+  using LA2 = DirectRows<256>;
+  using LB2 = DirectRows<128>;
+  Contraction<256, 128, LA1, LB1, LA2, LB2, Epi> cfg{};
+  cfg.a1 = LA1{dY, N, M};
+  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K};
+  cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.sg), w.r64, M};
+  cfg.b2 = LB2{apad, w.r64, K};
+  cfg.nP = (int)ceil_div(M, 256);
+  cfg.nQ = (int)ceil_div(K, 128);
+  cfg.S1 = (int)ceil_div(N, 64);
+  cfg.S2 = (int)(w.r64 / 64);
+  cfg.splits = 1;
+  cfg.steps_per_split = cfg.S1 + cfg.S2;
+  cfg.epi = epi;
+  if (Epi::kKeepSeg2 && cfg.S2 > 3) return hipErrorInvalidValue;  // rejected by the API
+  return run<256, 128, LA1, LB1, LA2, LB2, Epi, false>(cfg, stream);
+}
+
+// dA = X^T (s G) and dB^T = dY^T (s T): both contractions in one launch
+// (Aop[k][m] = X[m][k], Aop[n][m] = dY[m][n]; Bop[j][m] = (sG)^T[j][m],
+// (sT)^T[j][m]), then the split-order reduce.
+template <class LA>
+hipError_t adapter_grads(LA xa, LA ya, int64_t M, int64_t N, int64_t K, int r, const WsLayout& w,
+                         char* ws, float* dA, float* dB, hipStream_t stream) {
+  using LB = DirectRows<64>;
+  using C = Contraction<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial>;
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  const int64_t splits = grad_splits(M, N, K, w.r64);
+  const int64_t steps = ceil_div(M, 64);
+  float* pa = part;
+  float* pb = part + K * w.r64 * splits;
+  C ca{}, cb{};
+  ca.a1 = xa;
+  ca.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.sgt), w.Mp, w.r64};
+  ca.nP = (int)ceil_div(K, 128);
+  ca.epi = EpiPartial{pa, K, w.r64};
+  cb.a1 = ya;
+  cb.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.stt), w.Mp, w.r64};
+  cb.nP = (int)ceil_div(N, 128);
+  cb.epi = EpiPartial{pb, N, w.r64};
+  for (C* c : {&ca, &cb}) {
+    c->nQ = (int)(w.r64 / 64);
+    c->S1 = (int)steps;
+    c->S2 = 0;
+    c->steps_per_split = (int)ceil_div(steps, splits);
+    c->splits = (int)ceil_div(steps, c->steps_per_split);
+  }
+  QLORA_TRY((run_pair<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial, true>(ca, cb, stream)));
+  hipLaunchKernelGGL(reduce_grads_kernel, dim3(grid_for((K + N) * (w.r64 / 4))), dim3(256), 0,
+                     stream, pa, pb, ca.splits, K, N, r, w.r64, dA, dB);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4Weight W,
                       const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                       int r, float scale, uint16_t* dX, float* dA, float* dB, void* ws_,
-                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1, Dropout dr) {
   char* ws = reinterpret_cast<char*>(ws_);
   const WsLayout w = ws_layout(M, N, K, r);
   float* part = reinterpret_cast<float*>(ws + w.part);
@@ -382,9 +485,11 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   {
     int splits = 0;
     DirectRows<64> lb{B, N, (int64_t)r};
-    QLORA_TRY(lowrank_partials(dY, N, M, N, lb, w.r64, part, &splits, stream));
-    const LowrankJob jg{part, splits, w.r64, nullptr, reinterpret_cast<uint16_t*>(ws + w.sg),
-                        reinterpret_cast<uint16_t*>(ws + w.sgt)};
+    QLORA_TRY(lowrank_partials(DirectRows<64>{dY, N, M}, M, N, lb, w.r64, part, &splits, stream));
+    // under dropout, s f G feeds both the masked dX columns and dA
+    LowrankJob jg{part, splits, w.r64, nullptr, reinterpret_cast<uint16_t*>(ws + w.sg),
+                  reinterpret_cast<uint16_t*>(ws + w.sgt)};
+    if (dr.mask) jg.f = dr.keep_scale;
     const LowrankJob jt = T ? LowrankJob{T, 1, (int64_t)r, nullptr, nullptr,
                                          reinterpret_cast<uint16_t*>(ws + w.stt)}
                             : LowrankJob{};
@@ -394,63 +499,28 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T, Nf4
   }
   if (!T) {
     QLORA_TRY(compute_T(X, A, M, K, r, w, ws, scale, reinterpret_cast<float*>(ws + w.t32),
-                        true, stream));
+                        true, dr, stream));
   }
-  // 3. dX = dY W' + (s G) A^T
+  // 3. dX = dY W' + (s G) A^T   (+ keep o ((s f G) A^T) under dropout)
   if (dX) {
-    using LA1 = DirectRows<256>;
-    using LB1 = Nf4Cols<128>;
-    using LA2 = DirectRows<256>;
-    using LB2 = DirectRows<128>;
-    Contraction<256, 128, LA1, LB1, LA2, LB2, EpiBf16> cfg{};
-    cfg.a1 = LA1{dY, N, M};
-    cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K};
-    cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.sg), w.r64, M};
-    cfg.b2 = LB2{apad, w.r64, K};
-    cfg.nP = (int)ceil_div(M, 256);
-    cfg.nQ = (int)ceil_div(K, 128);
-    cfg.S1 = (int)ceil_div(N, 64);
-    cfg.S2 = (int)(w.r64 / 64);
-    cfg.splits = 1;
-    cfg.steps_per_split = cfg.S1 + cfg.S2;
-    cfg.epi = EpiBf16{dX, K, M, K};
     QLORA_TRY(record_if(ev0, stream));
-    QLORA_TRY((run<256, 128, LA1, LB1, LA2, LB2, EpiBf16, false>(cfg, stream)));
+    if (dr.mask)
+      QLORA_TRY(input_grad(dY, W, apad, M, N, K, w, ws, EpiBf16Keep{dX, K, M, K, dr.mask, K / 32},
+                           stream));
+    else
+      QLORA_TRY(input_grad(dY, W, apad, M, N, K, w, ws, EpiBf16{dX, K, M, K}, stream));
     QLORA_TRY(record_if(ev1, stream));
   }
   // 4. dA = X^T (s G) (P = K) and dB^T = dY^T (s T) (P = N): Q = r64,
-  //    contraction over M, one launch for both, then one reduce
-  {
-    using LA = ColsBf16<128>;    // Aop[k][m] = X[m][k], Aop[n][m] = dY[m][n]
-    using LB = DirectRows<64>;   // Bop[j][m] = (sG)^T[j][m], (sT)^T[j][m]
-    using C = Contraction<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial>;
-    const int64_t splits = grad_splits(M, N, K, w.r64);
-    const int64_t steps = ceil_div(M, 64);
-    float* pa = part;
-    float* pb = part + K * w.r64 * splits;
-    C ca{}, cb{};
-    ca.a1 = LA{X, K, M, K};
-    ca.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.sgt), w.Mp, w.r64};
-    ca.nP = (int)ceil_div(K, 128);
-    ca.epi = EpiPartial{pa, K, w.r64};
-    cb.a1 = LA{dY, N, M, N};
-    cb.b1 = LB{reinterpret_cast<const uint16_t*>(ws + w.stt), w.Mp, w.r64};
-    cb.nP = (int)ceil_div(N, 128);
-    cb.epi = EpiPartial{pb, N, w.r64};
-    for (C* c : {&ca, &cb}) {
-      c->nQ = (int)(w.r64 / 64);
-      c->S1 = (int)steps;
-      c->S2 = 0;
-      c->steps_per_split = (int)ceil_div(steps, splits);
-      c->splits = (int)ceil_div(steps, c->steps_per_split);
-    }
-    QLORA_TRY((run_pair<128, 64, LA, LB, LoadNone, LoadNone, EpiPartial, true>(ca, cb, stream)));
-    hipLaunchKernelGGL(reduce_grads_kernel, dim3(grid_for((K + N) * (w.r64 / 4))), dim3(256), 0,
-                       stream, pa, pb,
-                       ca.splits, K, N, r, w.r64, dA, dB);
-    QLORA_TRY(hipGetLastError());
+  //    contraction over M, one launch for both, then one reduce; under
+  //    dropout the X operand passes through the keep mask (D(X)^T (s f G))
+  if (dr.mask) {
+    using LA = ColsBf16<128, true>;
+    return adapter_grads(LA{X, K, M, K, dr.mask, K / 32}, LA{dY, N, M, N, nullptr, 0}, M, N, K,
+                         r, w, ws, dA, dB, stream);
   }
-  return hipSuccess;
+  return adapter_grads(ColsBf16<128>{X, K, M, K}, ColsBf16<128>{dY, N, M, N}, M, N, K, r, w, ws,
+                       dA, dB, stream);
 }
 
 // exported for the small-M path, which shares the workspace layout

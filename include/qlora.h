@@ -73,6 +73,8 @@ enum {
 #define QLORA_NF4_BLOCK 64
 #define QLORA_NF4_GROUP 256
 #define QLORA_MAX_RANK 256
+/* Largest adapter rank of qlora_linear_bwd_dropout with an input gradient. */
+#define QLORA_MAX_DROPOUT_RANK 192
 
 /* ---- sizes of the NF4 store (host functions, no GPU work) ---------------- */
 
@@ -255,6 +257,72 @@ int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X,
                               uint16_t* dX, float* dA, float* dB, void* ws,
                               size_t ws_bytes, void* stream, void* ev_begin,
                               void* ev_end);
+
+/* ---- LoRA dropout -------------------------------------------------------------
+ * Dropout on the input of the adapter path only (ozercemkelahmet.com
+ * "QLoRA": the code section's LoraConfig trains with lora_dropout = 0.05;
+ * "Practical guidance and best practices": light dropout for small
+ * datasets). With a keep mask over X and f the inverse keep probability,
+ *   D(X) = (X o keep) f,   Y = X bf16(W')^T + scale * (D(X) A) B,
+ * the frozen-weight product sees X unchanged (inverted dropout).
+ *
+ * Keep mask: uint32 [M][K/32], bit j of word w of row m is element
+ * (m, 32 w + j); 1 = kept. qlora_dropout_mask draws it; a caller that needs
+ * the mask again (the backward, or a recomputed forward under gradient
+ * checkpointing) may keep it (M K / 8 bytes) or draw it again from the same
+ * seed and offset.
+ *
+ * Drop probability realized: thr / 2^16 with thr = floor(p 2^16 + 1/2)
+ * (0.0500030518 for p = 0.05); f = 2^16 / (2^16 - thr), rounded to float. */
+
+/* qlora_dropout_mask — keep mask of an [M x K] adapter input.
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC'11) with key = seed (low word
+ * first) and counter = (g mod 2^32, g div 2^32, offset mod 2^32,
+ * offset div 2^32) for group g of eight consecutive elements of X in
+ * row-major order; output word w gives the 16-bit values of elements
+ * 8g + 2w (low half) and 8g + 2w + 1 (high half); an element is kept when
+ * its value is at least thr. The mask of a given (seed, offset, p) depends
+ * only on each element's flat index m K + k.
+ *   mask   device uint32 [M x K/32] output
+ * Errors: INVALID_ARG (null mask, M or K not positive, p outside [0, 1) or
+ * NaN); UNSUPPORTED (K not a multiple of 32, p rounding to thr = 2^16,
+ * M K above 2^40, mask not 4-byte aligned). */
+int qlora_dropout_mask(int64_t M, int64_t K, float p, uint64_t seed, uint64_t offset,
+                       uint32_t* mask, void* stream);
+
+/* qlora_linear_fwd_dropout — qlora_linear_fwd with LoRA dropout:
+ *   Y = X bf16(W')^T + scale * T B,   T = D(X) A
+ *   keep_mask  device uint32 [M x K/32] from qlora_dropout_mask (p the same)
+ *   T_out      optional: T = D(X) A, which qlora_linear_bwd_dropout takes
+ * Every M takes the MFMA path (the mask enters the X A contraction).
+ * Errors: as qlora_linear_fwd; INVALID_ARG also for a null keep_mask or p
+ * outside [0, 1); UNSUPPORTED for p rounding to certain dropping or a
+ * keep_mask not 4-byte aligned. */
+int qlora_linear_fwd_dropout(const uint16_t* X, const uint8_t* codes,
+                             const uint8_t* absmax_q, const float* absmax_s2,
+                             const uint16_t* A, const uint16_t* B, int64_t M,
+                             int64_t N, int64_t K, int32_t r, float scale,
+                             const uint32_t* keep_mask, float p, uint16_t* Y,
+                             float* T_out, void* ws, size_t ws_bytes, void* stream);
+
+/* qlora_linear_bwd_dropout — qlora_linear_bwd with LoRA dropout (the chain
+ * rule through D):
+ *   G  = dY B^T
+ *   dX = dY bf16(W') + scale * ((G A^T) o keep) f
+ *   dA = scale * D(X)^T G,   dB = scale * T^T dY,   T = D(X) A
+ *   T  the forward's T_out, or NULL to recompute it from X and the mask
+ * Errors: as qlora_linear_bwd and qlora_linear_fwd_dropout; UNSUPPORTED
+ * also for r above QLORA_MAX_DROPOUT_RANK when dX is requested (the masked
+ * adapter columns of dX are summed from LDS stages that hold at most three
+ * 64-wide rank steps). */
+int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* X, const float* T,
+                             const uint8_t* codes, const uint8_t* absmax_q,
+                             const float* absmax_s2, const uint16_t* A,
+                             const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                             int32_t r, float scale, const uint32_t* keep_mask, float p,
+                             uint16_t* dX, float* dA, float* dB, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* ---- diagnostics ------------------------------------------------------------ */
 

@@ -155,3 +155,42 @@ def test_adamw_rejects(lib):
     assert a(*bad) == -1
     bad = list(ok); bad[1] = ODD
     assert a(*bad) == -2
+
+
+def test_dropout_mask_rejects(lib):
+    m = lib.qlora_dropout_mask
+    assert m(4, 64, 0.05, 1, 0, None, None) == -1          # null mask
+    assert m(0, 64, 0.05, 1, 0, FAKE, None) == -1          # M
+    assert m(4, 64, -0.1, 1, 0, FAKE, None) == -1          # p < 0
+    assert m(4, 64, 1.0, 1, 0, FAKE, None) == -1           # p = 1
+    assert m(4, 64, float("nan"), 1, 0, FAKE, None) == -1
+    assert m(4, 48, 0.05, 1, 0, FAKE, None) == -2          # K % 32
+    assert m(4, 64, 0.99999994, 1, 0, FAKE, None) == -2    # rounds to certain dropping
+    assert m(4, 64, 0.05, 1, 0, ODD, None) == -2           # alignment
+
+
+def test_linear_dropout_rejects(lib):
+    f = lib.qlora_linear_fwd_dropout
+    fa = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128, 128, 8, 1.0, FAKE, 0.05, FAKE, None, FAKE,
+          1 << 30, None]
+    bad = list(fa); bad[11] = None     # keep mask
+    assert f(*bad) == -1
+    bad = list(fa); bad[12] = 1.5      # p
+    assert f(*bad) == -1
+    bad = list(fa); bad[11] = ODD
+    assert f(*bad) == -2
+    bad = list(fa); bad[8] = 96        # K % 64
+    assert f(*bad) == -2
+    bad = list(fa); bad[16] = 8        # workspace
+    assert f(*bad) == -3
+    b = lib.qlora_linear_bwd_dropout
+    ba = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128, 128, 8, 1.0, FAKE, 0.05, FAKE,
+          FAKE, FAKE, FAKE, 1 << 30, None]
+    bad = list(ba); bad[13] = None
+    assert b(*bad) == -1
+    bad = list(ba); bad[11] = 256      # masked input gradient above rank 192
+    assert b(*bad) == -2
+    bad = list(ba); bad[14] = -0.5
+    assert b(*bad) == -1
+    bad = list(ba); bad[19] = 8
+    assert b(*bad) == -3
