@@ -36,6 +36,13 @@ int check_linear_shape(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (K % QLORA_NF4_BLOCK != 0 || N % QLORA_NF4_BLOCK != 0) return QLORA_ERR_UNSUPPORTED;
   if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return QLORA_ERR_UNSUPPORTED;
+  // The kernels address their operands with 32-bit buffer offsets: every
+  // bf16 activation matrix stays below 2^30 elements (2 GiB), the NF4 codes
+  // below 2 GiB, and a row below 2^21 elements (a 256-row tile spans at most
+  // 1 GiB).
+  if (N > (int64_t)1 << 21 || K > (int64_t)1 << 21) return QLORA_ERR_UNSUPPORTED;
+  if (M * N >= (int64_t)1 << 30 || M * K >= (int64_t)1 << 30 || N * K >= (int64_t)1 << 32)
+    return QLORA_ERR_UNSUPPORTED;
   return QLORA_OK;
 }
 

@@ -181,7 +181,8 @@ int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, fl
  * Workspace: `ws` is device memory of at least
  *   qlora_linear_workspace_bytes(M, N, K, r)
  * bytes, 256-byte aligned, owned by the caller; it may be reused between
- * calls that do not overlap. Its contents on entry do not matter. */
+ * calls that do not overlap. Its contents on entry do not matter. The query
+ * returns 0 for a shape or rank that the linear calls reject. */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 
 /* qlora_linear_fwd — Y = X bf16(W')^T + scale * (X A) B
@@ -199,9 +200,11 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  * memory-bound split-K GEMV path (two launches); larger M takes an MFMA
  * GEMM path. Calls capture into a HIP graph (no memset, no allocation).
  * Errors: INVALID_ARG (null X/codes/absmax/A/B/Y, non-positive M, N, K);
- * UNSUPPORTED (K or N not a multiple of 64, r outside [1, 256], M, N or K
- * above 2^30; codes, X or B not 16-byte aligned, A or Y not 2-byte aligned,
- * absmax_s2 or T_out not 4-byte aligned, ws not 256-byte aligned);
+ * UNSUPPORTED (K or N not a multiple of 64, r outside [1, 256], M above
+ * 2^30, N or K above 2^21, M N or M K at or above 2^30, N K at or above
+ * 2^32 (the kernels address operands with 32-bit offsets); codes, X or B
+ * not 16-byte aligned, A or Y not 2-byte aligned, absmax_s2 or T_out not
+ * 4-byte aligned, ws not 256-byte aligned);
  * WORKSPACE (ws NULL or ws_bytes below the query). */
 int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes,
                      const uint8_t* absmax_q, const float* absmax_s2,

@@ -102,6 +102,12 @@ def test_linear_fwd_rejects(lib):
     assert _fwd(lib, X=ODD) == -2
     assert _fwd(lib, ws=None) == -3
     assert _fwd(lib, wsb=16) == -3
+    # 32-bit operand offsets inside the kernels
+    assert _fwd(lib, M=1 << 20, N=1024, K=64) == -2        # M N = 2^30
+    assert _fwd(lib, M=1 << 20, N=64, K=1024) == -2        # M K = 2^30
+    assert _fwd(lib, M=1, N=(1 << 21) + 64, K=64) == -2    # N above 2^21
+    assert _fwd(lib, M=1, N=1 << 21, K=1 << 11) == -2      # N K = 2^32
+    assert lib.qlora_linear_workspace_bytes(1, 1 << 21, 1 << 11, 8) == 0
 
 
 def test_linear_bwd_rejects(lib):
