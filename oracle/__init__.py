@@ -27,6 +27,7 @@ from .nf4 import (  # noqa: F401
     nearest_level,
     quantize,
     dequantize,
+    dequantize_nodq,
     unpack_codes,
     pack_codes,
     num_blocks,

@@ -36,6 +36,15 @@ What is computed, and where the pages say so:
   Pinned by the 0.37-bit saving the pages state (closed form 0.373046875),
   by q8 = 255 at the group maximum and by the half-step error bound.
 
+* Without double quantization ([P4] "Step 2: store the scale per block": a
+  32-bit constant per block of 64, half a bit per weight) the store keeps
+  each block's float32 constant c itself, and w' = fl32(L4[q] * c); the
+  level-1 codes are the same as with double quantization. Pinned by the
+  worked example's printed values, an exact rational recomputation of
+  single elements, the half-gap error bound and agreement with the
+  double-quantized value wherever c' = c (a block that holds its group's
+  maximum).
+
 * Dequantization. c' = fl32(L8[q8] * s2), w' = fl32(L4[q] * c') with
   L8[k] = fl32(k / 255) ([P4] "A worked example" step 4, "Step 5: forward
   pass with on-the-fly dequantization"). Pinned by the worked example
@@ -256,3 +265,13 @@ def dequantize(codes, absmax_q, absmax_s2, numel):
     cprime = (l8[q8] * s2[g]).astype(np.float32)           # fl32(L8[q8] * s2)
     blk = np.arange(numel) // BLOCK
     return (levels[q] * cprime[blk]).astype(np.float32)    # fl32(L4[q] * c')
+
+
+def dequantize_nodq(codes, absmax, numel):
+    """Reconstruct float32 w' from a store without double quantization:
+    w' = fl32(L4[q] * c), c the float32 constant of the element's block."""
+    levels = codebook()
+    q = unpack_codes(codes, numel)
+    c = np.asarray(absmax, dtype=np.float32)
+    blk = np.arange(numel) // BLOCK
+    return (levels[q] * c[blk]).astype(np.float32)
