@@ -365,6 +365,28 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     qb.record()
     torch.cuda.synchronize()
     mkms = qa.elapsed_time(qb) / 10
+    # the plain step on stores without double quantization
+    nodq = [q.qlora_nf4_quantize(pr["W"], double_quant=False) for pr in projs]
+
+    def nstep():
+        for pr, st in zip(projs, nodq):
+            q.qlora_linear_fwd(pr["X"], st, pr["A"], pr["B"], s, Y=pr["Y"], T=pr["T"], ws=ws)
+            q.qlora_linear_bwd(pr["dY"], pr["X"], pr["T"], st, pr["A"], pr["B"], s, dX=pr["dX"],
+                               dA=pr["dA"], dB=pr["dB"], ws=ws)
+
+    for _ in range(args.warmup):
+        nstep()
+    torch.cuda.synchronize()
+    qa.record()
+    for _ in range(args.steps):
+        nstep()
+    qb.record()
+    torch.cuda.synchronize()
+    nms = qa.elapsed_time(qb) / args.steps
+    res["nodq"] = dict(ms_per_step=nms, tflops=flops_step / (nms * 1e-3) / 1e12,
+                       store_bytes=sum(st.nbytes() for st in nodq),
+                       dq_store_bytes=sum(pr["st"].nbytes() for pr in projs))
+    del nodq
     res["dropout"] = dict(p=pd, ms_per_step=dms, tflops=flops_step / (dms * 1e-3) / 1e12,
                           mask_shape=[M, 11008], mask_ms=mkms,
                           mask_Gelem_per_s=M * 11008 / (mkms * 1e-3) / 1e9)
@@ -390,7 +412,7 @@ def run_gemv(args, q, synthetic, torch, dev):
     wbytes = stores[0].nbytes()
     out = {"weight_bytes_per_call": wbytes, "stores": nstores,
            "rotating_bytes": wbytes * nstores, "timing": "HIP graph replay of back-to-back calls"}
-    for M in (1, 4, 16):
+    def call_time(M, stores):
         X = synthetic.normal((M, K), 1.0, dev, 0, synthetic.X_IDX)
         Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         ws = torch.empty(q.qlora_linear_workspace_bytes(M, N, K, r), dtype=torch.uint8,
@@ -415,7 +437,10 @@ def run_gemv(args, q, synthetic, torch, dev):
             g.replay()
         t1.record()
         torch.cuda.synchronize()
-        call_us = t0.elapsed_time(t1) * 1e3 / (args.gemv_rounds * nstores)
+        return t0.elapsed_time(t1) * 1e3 / (args.gemv_rounds * nstores)
+
+    for M in (1, 4, 16):
+        call_us = call_time(M, stores)
         gbps = wbytes / (call_us * 1e-6) / 1e9
         out[f"M{M}"] = dict(call_us=round(call_us, 3), eff_weight_GBps=round(gbps, 1),
                             roofline={"bound": "hbm", "achieved": round(gbps, 1),
@@ -423,7 +448,19 @@ def run_gemv(args, q, synthetic, torch, dev):
                                       "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                       "per": "call (main + epilogue launch)"})
         log(f"[gemv] M={M}: {call_us:.2f} us/call, {gbps:.0f} GB/s effective weight")
-        del g
+    # the same calls on stores without double quantization (float32 block
+    # constants, 4.5 bits per weight)
+    del stores
+    stores = []
+    for i in range(nstores):
+        W = synthetic.normal((N, K), 0.02, dev, 100 + i, synthetic.W_IDX)
+        stores.append(q.qlora_nf4_quantize(W, double_quant=False))
+        del W
+    nb = stores[0].nbytes()
+    us1 = call_time(1, stores)
+    out["nodq_M1"] = dict(call_us=round(us1, 3), weight_bytes_per_call=nb,
+                          eff_weight_GBps=round(nb / (us1 * 1e-6) / 1e9, 1))
+    log(f"[gemv] no double quantization, M=1: {us1:.2f} us/call")
     del stores
     return out
 
@@ -560,6 +597,7 @@ def main():
         "merge": pre["merge"],
         "adamw": pre["adamw"],
         "dropout": pre["dropout"],
+        "nodq": pre["nodq"],
         "gemv": gemv,
         "cpu_baseline": cpu,
     }

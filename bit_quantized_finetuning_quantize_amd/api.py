@@ -58,28 +58,40 @@ def qlora_nf4_codebook():
 
 
 class Nf4Store:
-    """The three device buffers of one NF4 tensor (owned by torch)."""
+    """The device buffers of one NF4 tensor (owned by torch). Without double
+    quantization `absmax_q` is None and `absmax_s2` holds one float32
+    constant per 64-block."""
 
     def __init__(self, codes, absmax_q, absmax_s2, numel, shape=None):
         self.codes, self.absmax_q, self.absmax_s2 = codes, absmax_q, absmax_s2
         self.numel = int(numel)
         self.shape = tuple(shape) if shape is not None else (self.numel,)
 
+    @property
+    def double_quant(self):
+        return self.absmax_q is not None
+
     def nbytes(self):
-        return self.codes.numel() + self.absmax_q.numel() + 4 * self.absmax_s2.numel()
+        q8 = self.absmax_q.numel() if self.absmax_q is not None else 0
+        return self.codes.numel() + q8 + 4 * self.absmax_s2.numel()
 
 
-def empty_store(numel, device, shape=None):
+def empty_store(numel, device, shape=None, double_quant=True):
     codes = torch.empty(qlora_nf4_codes_bytes(numel), dtype=torch.uint8, device=device)
-    q8 = torch.empty(qlora_nf4_num_blocks(numel), dtype=torch.uint8, device=device)
-    s2 = torch.empty(qlora_nf4_num_groups(numel), dtype=torch.float32, device=device)
+    if double_quant:
+        q8 = torch.empty(qlora_nf4_num_blocks(numel), dtype=torch.uint8, device=device)
+        s2 = torch.empty(qlora_nf4_num_groups(numel), dtype=torch.float32, device=device)
+    else:
+        q8 = None
+        s2 = torch.empty(qlora_nf4_num_blocks(numel), dtype=torch.float32, device=device)
     return Nf4Store(codes, q8, s2, numel, shape)
 
 
-def qlora_nf4_quantize(w, out=None):
-    """Quantize a bf16 tensor (any shape, flattened row-major)."""
+def qlora_nf4_quantize(w, out=None, double_quant=True):
+    """Quantize a bf16 tensor (any shape, flattened row-major); with
+    double_quant=False the store keeps the float32 block constants."""
     _need(w, torch.bfloat16, "w")
-    st = out if out is not None else empty_store(w.numel(), w.device, w.shape)
+    st = out if out is not None else empty_store(w.numel(), w.device, w.shape, double_quant)
     _check(LIB.qlora_nf4_quantize(_ptr(w), w.numel(), _ptr(st.codes), _ptr(st.absmax_q),
                                   _ptr(st.absmax_s2), _stream()))
     return st

@@ -25,8 +25,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kMaxGroups = 0x7fffffffLL;  // grid limit of the quantize launch
 
+// absmax_q may be null: a store without double quantization
 int check_store(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2) {
-  if (!codes || !absmax_q || !absmax_s2) return QLORA_ERR_INVALID_ARG;
+  (void)absmax_q;
+  if (!codes || !absmax_s2) return QLORA_ERR_INVALID_ARG;
   if (!aligned(codes, 16) || !aligned(absmax_s2, 4)) return QLORA_ERR_UNSUPPORTED;
   return QLORA_OK;
 }
@@ -85,7 +87,7 @@ void qlora_nf4_codebook(float* levels) {
 int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
                        float* absmax_s2, void* stream) {
   if (!w || numel <= 0) return QLORA_ERR_INVALID_ARG;
-  if (!codes || !absmax_q || !absmax_s2) return QLORA_ERR_INVALID_ARG;
+  if (!codes || !absmax_s2) return QLORA_ERR_INVALID_ARG;  // absmax_q null: no DQ
   if (!aligned(w, 2) || !aligned(codes, 4) || !aligned(absmax_s2, 4)) return QLORA_ERR_UNSUPPORTED;
   if (qlora_nf4_num_groups(numel) > kMaxGroups) return QLORA_ERR_UNSUPPORTED;
   return hip_status(qlora::launch_nf4_quantize(w, numel, codes, absmax_q, absmax_s2,
@@ -94,7 +96,7 @@ int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t
 
 static int dequant_common(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
                           int64_t numel, void* out, bool bf16, void* stream) {
-  if (!codes || !absmax_q || !absmax_s2 || !out || numel <= 0) return QLORA_ERR_INVALID_ARG;
+  if (!codes || !absmax_s2 || !out || numel <= 0) return QLORA_ERR_INVALID_ARG;
   if (!aligned(codes, 4) || !aligned(absmax_s2, 4) || !aligned(out, 16)) return QLORA_ERR_UNSUPPORTED;
   return hip_status(qlora::launch_nf4_dequantize(codes, absmax_q, absmax_s2, numel, out, bf16,
                                                  reinterpret_cast<hipStream_t>(stream)));

@@ -297,6 +297,19 @@ struct ColsBf16 {
   }
 };
 
+// Where the two NF4 loaders find a block's constant. With double
+// quantization: 8-bit code absmax_q[b] and second-level constant
+// absmax_s2[b >> 8]. Without it (absmax_q null): absmax_s2[b] is the float32
+// constant itself, read through the same path with the group shift 0 and the
+// 8-bit code forced to 255, since fl(fl(255/255) c) = fl(1 c) = c exactly.
+struct Nf4Consts {
+  int gshift = 8;      // log2 of the blocks per second-level constant
+  uint32_t q8or = 0u;  // 255 without double quantization
+  __device__ __forceinline__ int64_t s2_bytes(int64_t nblocks) const {
+    return ((nblocks + (1ll << gshift) - 1) >> gshift) * 4;
+  }
+};
+
 // NF4 weight rows (forward): tile row i = weight row n0 + i (output
 // feature), contraction = input feature k; a step is one 64-block of each
 // row. Two producer threads per row, 32 codes each.
@@ -310,6 +323,7 @@ struct Nf4Rows {
   const uint8_t* absmax_q;
   const float* absmax_s2;
   int64_t N, K;
+  Nf4Consts cst;
   int64_t n0_;
   int vcode, vq;
   int blk0;  // block index of this thread's row at step 0 (< 2^31 by API limits)
@@ -325,12 +339,12 @@ struct Nf4Rows {
   __device__ __forceinline__ void load(int step, Regs& r, int) const {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + n0_ * (K / 2), (N - n0_) * (K / 2));
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(absmax_q + n0_ * (K / kBlock), (N - n0_) * (K / kBlock));
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(absmax_s2, ((N * K / kBlock) + kGroup - 1) / kGroup * 4);
+        absmax_q ? make_rsrc(absmax_q + n0_ * (K / kBlock), (N - n0_) * (K / kBlock))
+                 : make_rsrc(nullptr, 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(absmax_s2, cst.s2_bytes(N * K / kBlock));
     r.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vcode, step * 32, 0));
-    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step, 0);
-    const int g = (blk0 + step) >> 8;
+    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step, 0) | cst.q8or;
+    const int g = (blk0 + step) >> cst.gshift;
     r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, g * 4, 0, 0));
   }
   __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {
@@ -364,6 +378,7 @@ struct Nf4Cols {
   const uint8_t* absmax_q;
   const float* absmax_s2;
   int64_t N, K;
+  Nf4Consts cst;
   int vcode, vq;
   int blk0;  // block index of (row t % 64, this k range) at step 0
   struct Regs { u32x4 c; uint32_t q8; float s2; };
@@ -379,14 +394,13 @@ struct Nf4Cols {
   __device__ __forceinline__ void direct(int, uint32_t, int) const {}
   __device__ __forceinline__ void load(int step, Regs& r, int) const {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes, (N * K) / 2);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(absmax_q, (N * K) / kBlock);
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(absmax_s2, ((N * K / kBlock) + kGroup - 1) / kGroup * 4);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(absmax_q, absmax_q ? (N * K) / kBlock : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(absmax_s2, cst.s2_bytes(N * K / kBlock));
     const int kb = (int)(K / kBlock);
     r.c = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vcode, step * kStep * (int)(K / 2), 0));
-    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step * kStep * kb, 0);
-    const int g = (blk0 + step * kStep * kb) >> 8;
+    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step * kStep * kb, 0) | cst.q8or;
+    const int g = (blk0 + step * kStep * kb) >> cst.gshift;
     r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, g * 4, 0, 0));
   }
   __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {

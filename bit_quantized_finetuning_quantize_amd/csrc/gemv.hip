@@ -78,11 +78,12 @@ struct alignas(16) Shared {
 };
 
 // GEMV workgroup: weight rows [64 tile, 64 tile + 64), K split ks of kc =
-// I*128. Wave w owns 16 rows (row group w & 3) and one of the kKQ k groups
+// I*128. kDQ false: the store has no 8-bit codes and absmax_s2 holds one
+// float32 constant per block (one dword load per packet). Wave w owns 16 rows (row group w & 3) and one of the kKQ k groups
 // of the split (w >> 2); the groups are summed in a fixed order through LDS.
 // The split's token rows are staged once in LDS; every global load is
 // issued before any arithmetic.
-template <int I>
+template <int I, bool kDQ>
 __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
 #pragma clang fp contract(off)
   constexpr int kOut = 0x7ffffff0;  // an offset past every range: the load returns 0
@@ -98,9 +99,10 @@ __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
   const int kw = kq * (kc / kKQ);   // this wave's first k inside the split
 
   const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.codes, a.N * a.K / 2);
-  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.absmax_q, a.N * a.K / kBlock);
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.absmax_q, kDQ ? a.N * a.K / kBlock : 0);
   const __amdgpu_buffer_rsrc_t rs =
-      rsrc_of(a.absmax_s2, (a.N * a.K / kBlock + kGroup - 1) / kGroup * 4);
+      rsrc_of(a.absmax_s2, kDQ ? (a.N * a.K / kBlock + kGroup - 1) / kGroup * 4
+                               : a.N * a.K / kBlock * 4);
   const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.X, (int64_t)a.M * a.K * 2);
 
   // Every load is unconditional (an invalid one reads past the range and
@@ -137,15 +139,24 @@ __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
   const int64_t b0 = e0 / kBlock;
   constexpr int kQW = (2 * P + 1) / 4 + 1;
   uint32_t qw[kQW];
-#pragma unroll
-  for (int w = 0; w < kQW; ++w)
-    qw[w] = __builtin_amdgcn_raw_buffer_load_b32(rq, nok ? (int)((b0 & ~3LL) + 4 * w) : kOut, 0, 0);
-  // second-level constants: blocks b0 .. b0 + 2P - 2 span at most two groups
+  float s2a = 0.0f, s2b = 0.0f;
   const int64_t g0 = b0 / kGroup;
-  const float s2a = __builtin_bit_cast(
-      float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)(g0 * 4) : kOut, 0, 0));
-  const float s2b = __builtin_bit_cast(
-      float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)((g0 + 1) * 4) : kOut, 0, 0));
+  float cb[P];  // without double quantization: each packet's block constant
+  if constexpr (kDQ) {
+#pragma unroll
+    for (int w = 0; w < kQW; ++w)
+      qw[w] = __builtin_amdgcn_raw_buffer_load_b32(rq, nok ? (int)((b0 & ~3LL) + 4 * w) : kOut, 0, 0);
+    // second-level constants: blocks b0 .. b0 + 2P - 2 span at most two groups
+    s2a = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)(g0 * 4) : kOut, 0, 0));
+    s2b = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)((g0 + 1) * 4) : kOut, 0, 0));
+  } else {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      cb[p] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, nok ? (int)((b0 + 2 * p) * 4) : kOut, 0, 0));
+  }
   // lookup tables, built while the loads are in flight
   if (tid < 256) {
 #pragma clang fp contract(off)
@@ -162,11 +173,16 @@ __device__ void gemv_tile(const GemvArgs& a, int tile, int ks, Shared<I>& sh) {
   floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const int64_t b = b0 + 2 * p;
-    const int qi = (int)(b - (b0 & ~3LL));
-    const uint32_t q8 = (qw[qi >> 2] >> (8 * (qi & 3))) & 0xffu;
-    const float s2 = (b / kGroup == g0) ? s2a : s2b;
-    const float cs = sh.l8[q8] * s2;
+    float cs;
+    if constexpr (kDQ) {
+      const int64_t b = b0 + 2 * p;
+      const int qi = (int)(b - (b0 & ~3LL));
+      const uint32_t q8 = (qw[qi >> 2] >> (8 * (qi & 3))) & 0xffu;
+      const float s2 = (b / kGroup == g0) ? s2a : s2b;
+      cs = sh.l8[q8] * s2;
+    } else {
+      cs = cb[p];
+    }
     const int kl = kw + p * kChunk + 32 * g;  // this lane's k inside the split
     const PermTable pt = perm_table(cs);  // lookups by v_perm: no LDS round trips
 #pragma unroll
@@ -301,7 +317,7 @@ __device__ void adapter_tile(const GemvArgs& a, int chunk, int t, Shared<I>& sh)
 }
 
 // Adapter workgroups come first in the grid so that they start first.
-template <int I>
+template <int I, bool kDQ>
 __global__ void __launch_bounds__(kThreads) nf4_gemv_main(GemvArgs a) {
   __shared__ Shared<I> sh;
   const int id = blockIdx.x;
@@ -309,7 +325,7 @@ __global__ void __launch_bounds__(kThreads) nf4_gemv_main(GemvArgs a) {
   if (id < nadapt)
     adapter_tile<I>(a, id / a.tblocks, id % a.tblocks, sh);
   else
-    gemv_tile<I>(a, (id - nadapt) % a.ntiles, (id - nadapt) / a.ntiles, sh);
+    gemv_tile<I, kDQ>(a, (id - nadapt) % a.ntiles, (id - nadapt) / a.ntiles, sh);
 }
 
 // Y[m][n] = bf16( sum_s Py[s][m][n] + s * sum_j T[m][j] B[j][n] ),
@@ -490,7 +506,10 @@ hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A, co
   dim3 grid((unsigned)(a.ntiles * splits + a.tchunks * a.tblocks));
   hipError_t e = record_if(ev0, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_gemv_main<kIters>, grid, dim3(kThreads), 0, stream, a);
+  if (W.absmax_q)
+    hipLaunchKernelGGL((nf4_gemv_main<kIters, true>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((nf4_gemv_main<kIters, false>), grid, dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = record_if(ev1, stream);

@@ -316,6 +316,17 @@ hipError_t lowrank_partials(LA la, int64_t M, int64_t C, LB lb, int64_t r64, flo
   return run<64, 64, LA, LB, LoadNone, LoadNone, EpiPartial, true>(cfg, stream);
 }
 
+// The loaders' constant mode: double-quantized, or one float32 constant
+// per block when the store has no 8-bit codes.
+Nf4Consts nf4_consts(const Nf4Weight& W) {
+  Nf4Consts c;
+  if (!W.absmax_q) {
+    c.gshift = 0;
+    c.q8or = 255u;
+  }
+  return c;
+}
+
 #define QLORA_TRY(x)                       \
   do {                                     \
     hipError_t e_ = (x);                   \
@@ -388,7 +399,7 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
   using LB2 = ColsBf16<128>;
   Contraction<256, 128, LA1, LB1, LA2, LB2, EpiBf16> cfg{};
   cfg.a1 = LA1{X, K, M};
-  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K};
+  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K, nf4_consts(W)};
   cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.st), w.r64, M};
   cfg.b2 = LB2{B, N, (int64_t)r, N};  // Bop[n][j] = B[j][n]
   cfg.nP = (int)ceil_div(M, 256);
@@ -418,7 +429,7 @@ hipError_t input_grad(const uint16_t* dY, Nf4Weight W, const uint16_t* apad, int
   using LB2 = DirectRows<128>;
   Contraction<256, 128, LA1, LB1, LA2, LB2, Epi> cfg{};
   cfg.a1 = LA1{dY, N, M};
-  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K};
+  cfg.b1 = LB1{W.codes, W.absmax_q, W.absmax_s2, N, K, nf4_consts(W)};
   cfg.a2 = LA2{reinterpret_cast<const uint16_t*>(ws + w.sg), w.r64, M};
   cfg.b2 = LB2{apad, w.r64, K};
   cfg.nP = (int)ceil_div(M, 256);

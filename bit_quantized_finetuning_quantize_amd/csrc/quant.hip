@@ -1,4 +1,6 @@
 // NF4 quantization (with double quantization) and dequantization kernels.
+// A null absmax_q selects the store without double quantization (Step 2
+// alone): absmax_s2 then holds one float32 constant per block, c' = c.
 //
 // Quantization follows ozercemkelahmet.com "QLoRA", How it works, Step 1
 // (blocks of 64 scaled by their largest magnitude, each value replaced by
@@ -94,7 +96,7 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
                          fmaxf(s_wavemax[2], s_wavemax[3]));
 
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
-  {
+  if (absmax_q) {
     const int64_t b = group * kGroup + tid;
     if (b < nblocks) {
       uint32_t q8 = 0;
@@ -106,6 +108,10 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
       absmax_q[b] = (uint8_t)q8;
     }
     if (tid == 0) absmax_s2[group] = s2;
+  } else {
+    // no double quantization: the float32 block constants themselves
+    const int64_t b = group * kGroup + tid;
+    if (b < nblocks) absmax_s2[b] = s_blockmax[tid];
   }
 
   // first level: codes against the exact float32 block maximum
@@ -179,7 +185,7 @@ nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
         if (i * 4 + j < nbytes) word |= (uint32_t)codes[i * 4 + j] << (8 * j);
     }
     const int64_t b = e0 / kBlock;
-    const float cs = block_scale(absmax_q[b], absmax_s2[b / kGroup]);
+    const float cs = absmax_q ? block_scale(absmax_q[b], absmax_s2[b / kGroup]) : absmax_s2[b];
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = s_lv[(word >> (4 * j)) & 15u] * cs;
@@ -293,7 +299,7 @@ nf4_merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
     const int64_t e0 = n * K + k;                       // first of 8 elements, one block
     const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
     const int64_t b = e0 / kBlock;
-    const float cs = block_scale(absmax_q[b], absmax_s2[b / kGroup]);
+    const float cs = absmax_q ? block_scale(absmax_q[b], absmax_s2[b / kGroup]) : absmax_s2[b];
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {

@@ -50,6 +50,14 @@
  *   c'  = fl32( fl32(absmax_q[b] / 255) * absmax_s2[g] )
  *   w'  = fl32( NF4[code_i] * c' )
  * and the compute weight is bf16(w'), rounded to nearest even.
+ *
+ * The store without double quantization (ozercemkelahmet.com "QLoRA",
+ * Step 2 alone: one 32-bit constant per block, 4.5 bits per weight) is
+ * passed as absmax_q = NULL, and absmax_s2 then holds
+ *   absmax_s2 float [qlora_nf4_num_blocks(numel)]
+ *             the float32 constant (largest magnitude) of each block,
+ * so that c' = absmax_s2[b]. The codes are the same in both stores. Every
+ * entry point that takes a store accepts either form.
  */
 #ifndef QLORA_H
 #define QLORA_H
@@ -108,9 +116,11 @@ void qlora_nf4_codebook(float* levels);
  * level 0). Per group of 256 constants: s2 = max c and
  * absmax_q = round_half_even(255 * fl32(c / s2)) (0 when s2 = 0).
  * A short final block or group takes its maximum over the values present.
- * Errors: INVALID_ARG for a null pointer or numel <= 0; UNSUPPORTED if `w`
- * is not 2-byte aligned or `codes` / `absmax_s2` not 4-byte aligned. Needs
- * no workspace. */
+ * absmax_q = NULL writes the store without double quantization instead:
+ * absmax_s2 [ceil(numel/64)] receives each block's c (same codes).
+ * Errors: INVALID_ARG for a null w, codes or absmax_s2, or numel <= 0;
+ * UNSUPPORTED if `w` is not 2-byte aligned or `codes` / `absmax_s2` not
+ * 4-byte aligned. Needs no workspace. */
 int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_s2, void* stream);
 

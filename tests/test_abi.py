@@ -75,6 +75,8 @@ def test_quantize_rejects(lib):
     assert q(None, 64, FAKE, FAKE, FAKE, None) == -1
     assert q(FAKE, 0, FAKE, FAKE, FAKE, None) == -1
     assert q(FAKE, 64, None, FAKE, FAKE, None) == -1
+    assert q(FAKE, 64, FAKE, FAKE, None, None) == -1   # absmax_s2 is always needed
+    assert q(FAKE, 64, FAKE, None, None, None) == -1
     assert q(ODD, 64, FAKE, FAKE, FAKE, None) == -2
     assert q(FAKE, 64, ODD, FAKE, FAKE, None) == -2
 
