@@ -448,6 +448,41 @@ def run_gemv(args, q, synthetic, torch, dev):
                                       "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                       "per": "call (main + epilogue launch)"})
         log(f"[gemv] M={M}: {call_us:.2f} us/call, {gbps:.0f} GB/s effective weight")
+    # context for the per-call figures: one vectorized torch elementwise
+    # launch that reads the same number of bytes (an int64 view, compared
+    # with 0: one byte written per eight read) from 64 rotating buffers, in
+    # the same graph replay -- about the floor of a launch that streams a
+    # store of this size from HBM
+    bufs = [torch.zeros(wbytes // 8, dtype=torch.int64, device=dev) for _ in range(nstores)]
+    flags = torch.empty(wbytes // 8, dtype=torch.bool, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for b in bufs:
+            torch.ne(b, 0, out=flags)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs):
+        for b in bufs:
+            torch.ne(b, 0, out=flags)
+    gs.replay()
+    torch.cuda.synchronize()
+    ta = torch.cuda.Event(enable_timing=True)
+    tb = torch.cuda.Event(enable_timing=True)
+    ta.record()
+    for _ in range(args.gemv_rounds):
+        gs.replay()
+    tb.record()
+    torch.cuda.synchronize()
+    sus = ta.elapsed_time(tb) * 1e3 / (args.gemv_rounds * nstores)
+    sb = (wbytes // 8) * 8
+    out["stream_floor"] = dict(call_us=round(sus, 3), bytes_read=sb, bytes_written=sb // 8,
+                               GBps=round(sb / (sus * 1e-6) / 1e9, 1),
+                               what="torch.ne(int64 view, 0) over the store's bytes, "
+                                    "64 rotating buffers, HIP-graph replay")
+    log(f"[gemv] streaming floor (torch.ne over {sb} B): {sus:.2f} us per launch")
+    del gs, bufs, flags
     # the same calls on stores without double quantization (float32 block
     # constants, 4.5 bits per weight)
     del stores
