@@ -48,3 +48,5 @@ from .dropout import (  # noqa: F401
     pack_keep,
     unpack_keep,
 )
+from . import fp8  # noqa: F401
+from .adamw8 import BLOCK8, adamw8_step, dequantize_state, num_blocks8, quantize_state  # noqa: F401
