@@ -328,7 +328,27 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     ams = qa.elapsed_time(qb) / 5
     res["adamw"] = dict(params=na, ms=ams, bytes_per_param=30,
                         GBps=30 * na / (ams * 1e-3) / 1e9)
-    del st_p, st_m, st_v, st_g, st_16
+    del st_m, st_v
+    # the same step with 8-bit moments (codes and per-256 scales); a random
+    # gradient, so that every block encodes non-zero moments
+    st_g.normal_(0.0, 1e-3)
+    m8, sm8, v8, sv8 = q.adamw8_state(na, dev)
+    for t in range(1, 3):
+        q.qlora_adamw8_step(st_p, m8, sm8, v8, sv8, st_g, 2e-4, step=t, weight_decay=0.01,
+                            p_bf16=st_16)
+    torch.cuda.synchronize()
+    qa.record()
+    for t in range(3, 8):
+        q.qlora_adamw8_step(st_p, m8, sm8, v8, sv8, st_g, 2e-4, step=t, weight_decay=0.01,
+                            p_bf16=st_16)
+    qb.record()
+    torch.cuda.synchronize()
+    a8ms = qa.elapsed_time(qb) / 5
+    b8 = 18 + 16 / 256  # p, g, codes in and out, bf16 p, scales
+    res["adamw8"] = dict(params=na, ms=a8ms, bytes_per_param=round(b8, 4),
+                         GBps=b8 * na / (a8ms * 1e-3) / 1e9,
+                         state_bytes=2 * na + 8 * ((na + 255) // 256))
+    del m8, sm8, v8, sv8, st_p, st_g, st_16
     res["merge"] = dict(shape=[11008, 4096], rank=r, ms=mms,
                         GBps=(st0.nbytes() + 2 * W0.numel()) / (mms * 1e-3) / 1e9,
                         rank_flops_TFLOPs=2 * W0.numel() * r / (mms * 1e-3) / 1e12)
@@ -631,6 +651,7 @@ def main():
         "dequantize": pre["dequantize"],
         "merge": pre["merge"],
         "adamw": pre["adamw"],
+        "adamw8": pre["adamw8"],
         "dropout": pre["dropout"],
         "nodq": pre["nodq"],
         "gemv": gemv,

@@ -6,7 +6,9 @@ from .api import (  # noqa: F401
     GROUP,
     Nf4Store,
     QloraError,
+    adamw8_state,
     empty_store,
+    qlora_adamw8_step,
     qlora_adamw_step,
     qlora_dropout_mask,
     qlora_linear_bwd,

@@ -29,6 +29,8 @@ SIGNATURES = {
     "qlora_nf4_dequantize_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp, _vp]),
     "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_f32, _c_f32, _c_f32, _c_f32,
                                   _c_f32, _c_i64, _vp, _vp]),
+    "qlora_adamw8_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_f32, _c_f32, _c_f32,
+                                   _c_f32, _c_f32, _c_i64, _vp, _vp]),
     "qlora_nf4_merge": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i32, _c_f32, _vp,
                                  _vp]),
     "qlora_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i32]),

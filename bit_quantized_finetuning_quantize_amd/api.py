@@ -140,6 +140,37 @@ def qlora_adamw_step(p, m, v, g, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_de
                                 _ptr(p_bf16) if p_bf16 is not None else None, _stream()))
 
 
+def adamw8_state(n, device):
+    """Zero 8-bit AdamW state for n parameters: (m8, m_scale, v8, v_scale)."""
+    nb = (n + 255) // 256
+    return (torch.zeros(n, dtype=torch.uint8, device=device),
+            torch.zeros(nb, dtype=torch.float32, device=device),
+            torch.zeros(n, dtype=torch.uint8, device=device),
+            torch.zeros(nb, dtype=torch.float32, device=device))
+
+
+def qlora_adamw8_step(p, m8, m_scale, v8, v_scale, g, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                      weight_decay=0.0, step=1, p_bf16=None):
+    """One AdamW step with 8-bit moments (all tensors updated in place)."""
+    n = p.numel()
+    _need(p, torch.float32, "p")
+    _need(g, torch.float32, "g")
+    _need(m_scale, torch.float32, "m_scale")
+    _need(v_scale, torch.float32, "v_scale")
+    _need(m8, torch.uint8, "m8")
+    _need(v8, torch.uint8, "v8")
+    if g.numel() != n or m8.numel() != n or v8.numel() != n:
+        raise QloraError("p, g, m8 and v8 must have the same number of elements")
+    if m_scale.numel() != (n + 255) // 256 or v_scale.numel() != (n + 255) // 256:
+        raise QloraError("one scale per block of 256 parameters")
+    if p_bf16 is not None:
+        _need(p_bf16, torch.bfloat16, "p_bf16")
+    _check(LIB.qlora_adamw8_step(_ptr(p), _ptr(m8), _ptr(m_scale), _ptr(v8), _ptr(v_scale),
+                                 _ptr(g), n, float(lr), float(beta1), float(beta2), float(eps),
+                                 float(weight_decay), int(step),
+                                 _ptr(p_bf16) if p_bf16 is not None else None, _stream()))
+
+
 def qlora_linear_workspace_bytes(M, N, K, r):
     return int(LIB.qlora_linear_workspace_bytes(M, N, K, r))
 

@@ -1,4 +1,4 @@
-// AdamW step for the adapter parameters, float32 state.
+// AdamW step for the adapter parameters, float32 state or 8-bit state.
 //
 // The trained parameters of the method are the adapter matrices; the pages
 // name AdamW (32-bit or 8-bit state, paged) as their optimizer
@@ -82,11 +82,150 @@ adamw_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v
   }
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// 8-bit state. Each moment is held per block of 256 parameters as 8-bit
+// floating-point codes (OCP OFP8: E4M3 for m, E5M2 for v; sign, exponent
+// bias 7 / 15, 3 / 2 mantissa bits, subnormals) and one float32 scale:
+//   x' = fl(dec(code) * scale),   scale = fl(max_block |x| / top),
+//   code = enc(fl(x / scale)) (0 when scale = 0), top = 448 / 57344,
+// enc rounding to nearest, ties to the even code, saturating at top. One
+// wave owns one block: four parameters per lane, the block maxima by a
+// wave-wide reduction.
 
-hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n, float lr,
-                        float beta1, float beta2, float eps, float weight_decay, int64_t step,
-                        uint16_t* p16, hipStream_t stream) {
+// dec: the value of a code, exactly (the exponent field goes straight into
+// the float's exponent; subnormals are m 2^(1 - bias - mbits)).
+template <int kE, int kM, int kBias>
+__device__ __forceinline__ float ofp8_decode(uint32_t c) {
+  const uint32_t s = (c >> 7) & 1u;
+  const uint32_t e = (c >> kM) & ((1u << kE) - 1u);
+  const uint32_t m = c & ((1u << kM) - 1u);
+  const float sub = (float)m * __builtin_bit_cast(float, (uint32_t)(127 + 1 - kBias - kM) << 23);
+  const float nrm = __builtin_bit_cast(float, ((e + 127u - kBias) << 23) | (m << (23 - kM)));
+  const float mag = e ? nrm : sub;
+  return s ? -mag : mag;
+}
+
+// enc for a finite float: the mantissa rounded to kM bits on its integer
+// bits (ties to even), a carry running into the exponent field; values
+// below the smallest normal rounded on the subnormal grid.
+template <int kE, int kM, int kBias, uint32_t kTopCode>
+__device__ __forceinline__ uint32_t ofp8_encode(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 31) << 7;
+  const uint32_t ua = u & 0x7fffffffu;
+  const float a = __builtin_bit_cast(float, ua);
+  const float top = ofp8_decode<kE, kM, kBias>(kTopCode);
+  const float min_normal = __builtin_bit_cast(float, (uint32_t)(127 + 1 - kBias) << 23);
+  uint32_t mag;
+  if (!(a < top)) {
+    mag = kTopCode;
+  } else if (a < min_normal) {
+    // a 2^(bias - 1 + kM) is exact; rintf rounds half to even
+    mag = (uint32_t)__builtin_rintf(a * __builtin_bit_cast(float, (uint32_t)(127 - 1 + kBias + kM) << 23));
+  } else {
+    const uint32_t e = (ua >> 23) - 127u + kBias;     // biased exponent of the code
+    const uint32_t q = (ua >> (23 - kM)) & ((1u << kM) - 1u);
+    const uint32_t rem = ua & ((1u << (23 - kM)) - 1u);
+    const uint32_t half = 1u << (22 - kM);
+    const uint32_t up = (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+    mag = ((e << kM) + q + up);
+    mag = mag > kTopCode ? kTopCode : mag;
+  }
+  return mag | sign;
+}
+
+constexpr int kBlock8 = 256;
+
+template <bool kVec>
+__global__ void __launch_bounds__(256)
+adamw8_kernel(float* __restrict__ p, uint8_t* __restrict__ m8, float* __restrict__ sm,
+              uint8_t* __restrict__ v8, float* __restrict__ sv, const float* __restrict__ g,
+              int64_t n, AdamWConst k, uint16_t* __restrict__ p16) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int64_t nb = (n + kBlock8 - 1) / kBlock8;
+  // the block index is the same for every lane of a wave
+  for (int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); b < nb;
+       b += (int64_t)gridDim.x * 4) {
+    const int64_t e0 = b * kBlock8 + lane * 4;
+    float pv[4], gv[4];
+    uint32_t mc = 0, vc = 0;
+    const bool whole = e0 + 4 <= n;
+    if (kVec && whole) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(p + e0);
+      const floatx4 c = *reinterpret_cast<const floatx4*>(g + e0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { pv[j] = a[j]; gv[j] = c[j]; }
+      mc = *reinterpret_cast<const uint32_t*>(m8 + e0);
+      vc = *reinterpret_cast<const uint32_t*>(v8 + e0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pv[j] = 0.0f;
+        gv[j] = 0.0f;
+        if (e0 + j < n) {
+          pv[j] = p[e0 + j];
+          gv[j] = g[e0 + j];
+          mc |= (uint32_t)m8[e0 + j] << (8 * j);
+          vc |= (uint32_t)v8[e0 + j] << (8 * j);
+        }
+      }
+    }
+    const float smv = sm[b], svv = sv[b];
+    float mv[4], vv[4];
+    float am = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float m = ofp8_decode<4, 3, 7>((mc >> (8 * j)) & 0xffu) * smv;
+      float v = ofp8_decode<5, 2, 15>((vc >> (8 * j)) & 0xffu) * svv;
+      adamw_one(pv[j], m, v, gv[j], k);
+      mv[j] = m;
+      vv[j] = v;
+      if (e0 + j < n) {
+        am = fmaxf(am, fabsf(m));
+        av = fmaxf(av, v);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      am = fmaxf(am, __shfl_xor(am, off));
+      av = fmaxf(av, __shfl_xor(av, off));
+    }
+    const float smn = am / 448.0f;      // IEEE division
+    const float svn = av / 57344.0f;
+    uint32_t mo = 0, vo = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t cm = smn != 0.0f ? ofp8_encode<4, 3, 7, 0x7Eu>(mv[j] / smn) : 0u;
+      const uint32_t cv = svn != 0.0f ? ofp8_encode<5, 2, 15, 0x7Bu>(vv[j] / svn) : 0u;
+      mo |= cm << (8 * j);
+      vo |= cv << (8 * j);
+    }
+    if (kVec && whole) {
+      *reinterpret_cast<floatx4*>(p + e0) = floatx4{pv[0], pv[1], pv[2], pv[3]};
+      *reinterpret_cast<uint32_t*>(m8 + e0) = mo;
+      *reinterpret_cast<uint32_t*>(v8 + e0) = vo;
+      if (p16)
+        *reinterpret_cast<u32x2*>(p16 + e0) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (e0 + j >= n) continue;
+        p[e0 + j] = pv[j];
+        m8[e0 + j] = (uint8_t)(mo >> (8 * j));
+        v8[e0 + j] = (uint8_t)(vo >> (8 * j));
+        if (p16) p16[e0 + j] = (uint16_t)(pack_bf16x2(pv[j], 0.0f) & 0xffffu);
+      }
+    }
+    if (lane == 0) {
+      sm[b] = smn;
+      sv[b] = svn;
+    }
+  }
+}
+
+AdamWConst adamw_const(float lr, float beta1, float beta2, float eps, float weight_decay,
+                       int64_t step) {
   AdamWConst k;
   k.lr = lr;
   k.lw = (float)((double)lr * (double)weight_decay);
@@ -97,6 +236,35 @@ hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n,
   k.c1 = (float)(1.0 - std::pow((double)beta1, (double)step));
   k.c2 = (float)(1.0 - std::pow((double)beta2, (double)step));
   k.eps = eps;
+  return k;
+}
+
+}  // namespace
+
+hipError_t launch_adamw8(float* p, uint8_t* m8, float* sm, uint8_t* v8, float* sv, const float* g,
+                         int64_t n, float lr, float beta1, float beta2, float eps,
+                         float weight_decay, int64_t step, uint16_t* p16, hipStream_t stream) {
+  const AdamWConst k = adamw_const(lr, beta1, beta2, eps, weight_decay, step);
+  const bool vec = ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(g)) & 15) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(m8) | reinterpret_cast<uintptr_t>(v8)) & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p16) & 7) == 0;
+  const int64_t nb = (n + kBlock8 - 1) / kBlock8;
+  int64_t blocks = (nb + 3) / 4;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (vec)
+    hipLaunchKernelGGL(adamw8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, m8, sm,
+                       v8, sv, g, n, k, p16);
+  else
+    hipLaunchKernelGGL(adamw8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p, m8,
+                       sm, v8, sv, g, n, k, p16);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n, float lr,
+                        float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                        uint16_t* p16, hipStream_t stream) {
+  const AdamWConst k = adamw_const(lr, beta1, beta2, eps, weight_decay, step);
   const bool vec = n % 4 == 0 && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(m) |
                                    reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(g)) &
                                   15) == 0 &&

@@ -141,6 +141,21 @@ int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, fl
                                         p_bf16, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int qlora_adamw8_step(float* p, uint8_t* m8, float* m_scale, uint8_t* v8, float* v_scale,
+                      const float* g, int64_t n, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, int64_t step, uint16_t* p_bf16, void* stream) {
+  if (!p || !m8 || !m_scale || !v8 || !v_scale || !g || n <= 0 || step < 1)
+    return QLORA_ERR_INVALID_ARG;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f))
+    return QLORA_ERR_INVALID_ARG;
+  if (!aligned(p, 4) || !aligned(g, 4) || !aligned(m_scale, 4) || !aligned(v_scale, 4) ||
+      (p_bf16 && !aligned(p_bf16, 2)))
+    return QLORA_ERR_UNSUPPORTED;
+  return hip_status(qlora::launch_adamw8(p, m8, m_scale, v8, v_scale, g, n, lr, beta1, beta2, eps,
+                                         weight_decay, step, p_bf16,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (check_linear_shape(M, N, K, r) != QLORA_OK) return 0;
   return qlora::linear_workspace_bytes(M, N, K, r);

@@ -35,6 +35,13 @@ hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n,
                         float beta1, float beta2, float eps, float weight_decay, int64_t step,
                         uint16_t* p16, hipStream_t stream);
 
+// The same step with 8-bit moments: per block of 256 parameters, E4M3 codes
+// of m with scale sm[b] and E5M2 codes of v with scale sv[b] (updated in
+// place).
+hipError_t launch_adamw8(float* p, uint8_t* m8, float* sm, uint8_t* v8, float* sv, const float* g,
+                         int64_t n, float lr, float beta1, float beta2, float eps,
+                         float weight_decay, int64_t step, uint16_t* p16, hipStream_t stream);
+
 // ---- LoRA dropout -------------------------------------------------------------
 
 // Keep mask of an [M x K] adapter input (K a multiple of 32): Philox4x32-10

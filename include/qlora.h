@@ -183,6 +183,32 @@ int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, fl
                      float beta1, float beta2, float eps, float weight_decay, int64_t step,
                      uint16_t* p_bf16, void* stream);
 
+/* qlora_adamw8_step — qlora_adamw_step with 8-bit moments (the pages'
+ * recipe trains with a paged 8-bit AdamW: ozercemkelahmet.com "QLoRA", the
+ * code section's TrainingArguments and "Practical guidance and best
+ * practices", Optimizer and schedule; the pages do not say how the state is
+ * held in 8 bits). Each moment is kept per block of 256 parameters (block
+ * b = i / 256, the last one short) as 8-bit floating-point codes of the OCP
+ * 8-bit float formats and one float32 scale:
+ *   m8       device uint8 [n]            E4M3 codes of m (bias 7, max 448)
+ *   m_scale  device float [ceil(n/256)]  scale of m per block
+ *   v8       device uint8 [n]            E5M2 codes of v (bias 15, max 57344)
+ *   v_scale  device float [ceil(n/256)]  scale of v per block
+ * all zero before the first step. One step, every operation one float32
+ * operation rounded on its own:
+ *   m = dec(m8) * m_scale[b],  v = dec(v8) * v_scale[b]
+ *   the float32 AdamW step of qlora_adamw_step on (p, m, v, g)
+ *   m_scale[b] = max_block |m| / 448,   v_scale[b] = max_block v / 57344
+ *   m8 = enc(m / m_scale[b]),  v8 = enc(v / v_scale[b])  (0 when the scale is 0)
+ * enc rounds to the nearest code, ties to the even code, saturating at the
+ * largest finite one. 18 bytes of traffic per parameter against 30 for the
+ * float32 state (with the bf16 copy).
+ * Errors: as qlora_adamw_step (m8 and v8 need no alignment; the scales are
+ * float arrays). */
+int qlora_adamw8_step(float* p, uint8_t* m8, float* m_scale, uint8_t* v8, float* v_scale,
+                      const float* g, int64_t n, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, int64_t step, uint16_t* p_bf16, void* stream);
+
 /* ---- the linear layer ------------------------------------------------------
  * Shapes: X [M x K], frozen weight W [N x K] in the NF4 store (numel = N*K,
  * blocks run along K), A [K x r], B [r x N], Y and dY [M x N].

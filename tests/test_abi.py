@@ -202,3 +202,22 @@ def test_linear_dropout_rejects(lib):
     assert b(*bad) == -1
     bad = list(ba); bad[19] = 8
     assert b(*bad) == -3
+
+
+def test_adamw8_rejects(lib):
+    a = lib.qlora_adamw8_step
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 300, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None, None]
+    bad = list(ok); bad[1] = None      # m8
+    assert a(*bad) == -1
+    bad = list(ok); bad[4] = None      # v_scale
+    assert a(*bad) == -1
+    bad = list(ok); bad[6] = 0
+    assert a(*bad) == -1
+    bad = list(ok); bad[12] = 0        # step counts from 1
+    assert a(*bad) == -1
+    bad = list(ok); bad[9] = 1.0       # beta2 outside [0, 1)
+    assert a(*bad) == -1
+    bad = list(ok); bad[2] = ODD       # a scale array not 4-byte aligned
+    assert a(*bad) == -2
+    bad = list(ok); bad[13] = ODD      # bf16 copy not 2-byte aligned
+    assert a(*bad) == -2
