@@ -77,6 +77,21 @@ def test_ragged_shapes(q, shape):
     _run(q, M, N, K, r, 2 * r, seed=M + N + K)
 
 
+@pytest.mark.parametrize("shape", [
+    (300, 256, 320, 256),     # the largest rank: four LoRA steps on the MFMA paths
+    (200, 192, 256, 129),     # an odd rank padded to 192
+    (4, 256, 512, 256),       # the largest rank on the GEMV path
+    (16, 384, 256, 200),
+])
+@pytest.mark.parametrize("zero", [None, "W"])
+def test_large_ranks(q, shape, zero):
+    """Ranks up to the limit, with the workload's adapters and with W = 0
+    (where Y and dX are the adapter terms alone)."""
+    M, N, K, r = shape
+    _run(q, M, N, K, r, 2 * r, seed=M + r, zero=zero,
+         label=f"M={M} N={N} K={K} r={r}" + (" W=0" if zero else ""))
+
+
 @pytest.mark.parametrize("M", [8, 96])
 def test_adapter_only_when_weight_is_zero(q, M):
     """W = 0: Y is exactly the adapter term, so the LoRA path is checked at

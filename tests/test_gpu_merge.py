@@ -49,6 +49,8 @@ def _oracle_merge(st, N, K, A, B, scale, rows=None):
     (256, 512, 64, 0.25),    # several tiles, two rank chunks
     (192, 256, 40, 0.37),    # rank not a multiple of the 32-rank chunk
     (65, 192, 1, 1.0),       # rank one, one row past a tile
+    (128, 128, 256, 0.0625), # the largest rank: eight rank chunks
+    (96, 320, 129, 0.5),     # a chunk of one rank at the end
 ])
 def test_merge_bit_exact(q, N, K, r, scale):
     print(f"[case] merge N={N} K={K} r={r} s={scale}", flush=True)
