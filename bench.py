@@ -385,6 +385,34 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     qb.record()
     torch.cuda.synchronize()
     mkms = qa.elapsed_time(qb) / 10
+    # context: the step's two weight products done the unfused way, per
+    # projection a bf16 dequantization of the store and a vendor bf16 GEMM
+    # (torch.matmul on two 2-D tensors: hipBLASLt), for Y and again for dX
+    w16 = torch.empty(max(pr["N"] * pr["K"] for pr in projs), dtype=torch.bfloat16, device=dev)
+
+    def unfused():
+        for pr in projs:
+            W16 = q.qlora_nf4_dequantize_bf16(pr["st"], out=w16[:pr["N"] * pr["K"]])
+            W16 = W16.view(pr["N"], pr["K"])
+            torch.matmul(pr["X"], W16.t(), out=pr["Y"])
+            W16 = q.qlora_nf4_dequantize_bf16(pr["st"], out=w16[:pr["N"] * pr["K"]])
+            W16 = W16.view(pr["N"], pr["K"])
+            torch.matmul(pr["dY"], W16, out=pr["dX"])
+
+    for _ in range(args.warmup):
+        unfused()
+    torch.cuda.synchronize()
+    qa.record()
+    for _ in range(args.steps):
+        unfused()
+    qb.record()
+    torch.cuda.synchronize()
+    ums = qa.elapsed_time(qb) / args.steps
+    res["unfused_reference"] = dict(
+        ms=ums, fused_ms=sum(res["per_proj_fwd_ms"]) + sum(res["per_proj_dx_ms"]),
+        what="per projection: qlora_nf4_dequantize_bf16 + torch.matmul (hipBLASLt) for Y, and "
+             "again for dX; against the fused forward and dX kernels of the same step")
+    del w16
     # the plain step on stores without double quantization
     nodq = [q.qlora_nf4_quantize(pr["W"], double_quant=False) for pr in projs]
 
@@ -647,6 +675,11 @@ def main():
             "frac": round(pre["dx_kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(pre["dx_kernel_ms"], 4),
         },
+        "prefill_kernels_ms": {"fwd": [round(x, 4) for x in pre["per_proj_fwd_ms"]],
+                               "dx": [round(x, 4) for x in pre["per_proj_dx_ms"]],
+                               "order": ["gate 11008x4096", "up 11008x4096",
+                                         "down 4096x11008"]},
+        "unfused_reference": pre["unfused_reference"],
         "quantize": pre["quantize"],
         "dequantize": pre["dequantize"],
         "merge": pre["merge"],
