@@ -25,7 +25,9 @@
  * - bfloat16 tensors are passed as uint16_t bit patterns; float tensors are
  *   IEEE binary32. All matrices are dense, row-major, contiguous.
  * - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on
- *   it and the call returns without waiting.
+ *   it and the call returns without waiting. Calls enqueue kernel launches
+ *   only (no memset, no copy, no allocation, no synchronization), so any
+ *   sequence of them can be captured into a HIP graph and replayed.
  * - Return value: QLORA_OK (0) or a negative status. Arguments are validated
  *   before anything is enqueued; a failed validation has no side effects.
  *   QLORA_ERR_HIP means a launch failed; qlora_last_hip_error() then returns
