@@ -34,7 +34,10 @@
  *   the hipError_t of the calling thread's last failure. Nothing prints,
  *   throws or aborts.
  * - Calls that share a workspace buffer must not overlap in time (same
- *   stream, or caller-side ordering).
+ *   stream, or caller-side ordering). Otherwise calls are thread-safe: host
+ *   threads may call concurrently on their own streams with their own
+ *   buffers (the only process state is a per-device flag, set once under an
+ *   atomic, recording that a kernel's LDS limit has been raised).
  *
  * The NF4 store
  * -------------
