@@ -21,7 +21,7 @@
  * - Every pointer argument that names a tensor is a DEVICE pointer (memory of
  *   the GPU that is current on the calling thread) unless stated otherwise.
  *   The caller owns all memory; the library never allocates, frees or
- *   synchronizes, and keeps no state between calls.
+ *   synchronizes, and keeps no data between calls.
  * - bfloat16 tensors are passed as uint16_t bit patterns; float tensors are
  *   IEEE binary32. All matrices are dense, row-major, contiguous.
  * - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on
