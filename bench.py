@@ -408,8 +408,26 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     qb.record()
     torch.cuda.synchronize()
     ums = qa.elapsed_time(qb) / args.steps
+    # the vendor GEMM alone per projection (forward, then dX), 10 calls each
+    gemm_ms = []
+    for pr in projs:
+        W16 = q.qlora_nf4_dequantize_bf16(pr["st"], out=w16[:pr["N"] * pr["K"]])
+        W16 = W16.view(pr["N"], pr["K"])
+        pair = []
+        for fn in (lambda: torch.matmul(pr["X"], W16.t(), out=pr["Y"]),
+                   lambda: torch.matmul(pr["dY"], W16, out=pr["dX"])):
+            fn()
+            torch.cuda.synchronize()
+            qa.record()
+            for _ in range(10):
+                fn()
+            qb.record()
+            torch.cuda.synchronize()
+            pair.append(round(qa.elapsed_time(qb) / 10, 4))
+        gemm_ms.append(pair)
     res["unfused_reference"] = dict(
         ms=ums, fused_ms=sum(res["per_proj_fwd_ms"]) + sum(res["per_proj_dx_ms"]),
+        vendor_gemm_ms_fwd_dx=gemm_ms,
         what="per projection: qlora_nf4_dequantize_bf16 + torch.matmul (hipBLASLt) for Y, and "
              "again for dX; against the fused forward and dX kernels of the same step")
     del w16
