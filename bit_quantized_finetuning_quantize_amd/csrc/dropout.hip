@@ -1,8 +1,8 @@
 // Keep mask of LoRA dropout on the adapter input.
 //
-// ozercemkelahmet.com "QLoRA": the code section's LoraConfig trains with a
-// LoRA dropout of 0.05, and "Practical guidance and best practices" adds
-// light dropout for small datasets. Each element of the [M x K] adapter
+// ozercemkelahmet.com "QLoRA": the LoraConfig of "A code example with common
+// libraries" trains with a LoRA dropout of 0.05, and "Practical guidance and
+// best practices", Adapter settings, adds light dropout for small datasets. Each element of the [M x K] adapter
 // input is kept independently with probability 1 - thr / 2^16.
 //
 // Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel

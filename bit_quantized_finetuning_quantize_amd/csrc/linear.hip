@@ -21,8 +21,9 @@
 //                         dequantized and transposed into LDS
 //   4. dA = X^T (sG),  dB = (sT)^T dY   split-M contractions -> reduce
 //
-// LoRA dropout (ozercemkelahmet.com "QLoRA", the LoraConfig of the code
-// section and "Practical guidance and best practices"): the adapter path
+// LoRA dropout (ozercemkelahmet.com "QLoRA", the LoraConfig of "A code
+// example with common libraries"; "Practical guidance and best practices",
+// Adapter settings): the adapter path
 // takes D(X) = (X o keep) f, f the inverse keep probability, from a keep
 // mask over X. The mask is applied where X enters the T and dA products
 // (on the way into LDS) and, for dX, to the LoRA columns' contribution,

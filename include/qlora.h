@@ -189,9 +189,9 @@ int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, fl
                      uint16_t* p_bf16, void* stream);
 
 /* qlora_adamw8_step — qlora_adamw_step with 8-bit moments (the pages'
- * recipe trains with a paged 8-bit AdamW: ozercemkelahmet.com "QLoRA", the
- * code section's TrainingArguments and "Practical guidance and best
- * practices", Optimizer and schedule; the pages do not say how the state is
+ * recipe trains with a paged 8-bit AdamW: ozercemkelahmet.com "QLoRA",
+ * "A code example with common libraries", Training arguments, and "Practical
+ * guidance and best practices", Optimizer and schedule; the pages do not say how the state is
  * held in 8 bits). Each moment is kept per block of 256 parameters (block
  * b = i / 256, the last one short) as 8-bit floating-point codes of the OCP
  * 8-bit float formats and one float32 scale:
@@ -304,9 +304,9 @@ int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X,
 
 /* ---- LoRA dropout -------------------------------------------------------------
  * Dropout on the input of the adapter path only (ozercemkelahmet.com
- * "QLoRA": the code section's LoraConfig trains with lora_dropout = 0.05;
- * "Practical guidance and best practices": light dropout for small
- * datasets). With a keep mask over X and f the inverse keep probability,
+ * "QLoRA": the LoraConfig of "A code example with common libraries" trains
+ * with lora_dropout = 0.05; "Practical guidance and best practices", Adapter
+ * settings: light dropout for small datasets). With a keep mask over X and f the inverse keep probability,
  *   D(X) = (X o keep) f,   Y = X bf16(W')^T + scale * (D(X) A) B,
  * the frozen-weight product sees X unchanged (inverted dropout).
  *

@@ -1,7 +1,7 @@
 """AdamW step with 8-bit optimizer state (TEST INFRASTRUCTURE ONLY).
 
-The pages' recipe trains the adapters with a paged 8-bit AdamW ([P4] "Code:
-a QLoRA setup with Transformers and PEFT", TrainingArguments optim; "Practical
+The pages' recipe trains the adapters with a paged 8-bit AdamW ([P4] "A code
+example with common libraries", Training arguments, optim; "Practical
 guidance and best practices", Optimizer and schedule: a paged 8-bit or
 32-bit AdamW) and do not say how the state is held in 8 bits. Reading taken
 here: the pages' own scheme for the weights -- blocks with an absmax scale --

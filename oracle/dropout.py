@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY.
 
-The pages' training recipe sets a LoRA dropout of 0.05 ([P4] "Code: a QLoRA
-setup with Transformers and PEFT", LoraConfig; "Practical guidance and best
-practices", light dropout for small datasets). Reading taken here: inverted
+The pages' training recipe sets a LoRA dropout of 0.05 ([P4] "A code example
+with common libraries", its LoraConfig; "Practical guidance and best
+practices", Adapter settings: light dropout for small datasets). Reading taken here: inverted
 dropout on the input of the adapter path only, the frozen-weight product
 sees X unchanged:
 
