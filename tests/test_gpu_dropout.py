@@ -63,23 +63,28 @@ def test_mask_full_size(q):
     assert np.array_equal(got, want)
 
 
-def _run(q, M, N, K, r, alpha, p, seed=0, zero_w=False, label=None, T_given=True):
+def _run(q, M, N, K, r, alpha, p, seed=0, zero_w=False, label=None, T_given=True, dq=True):
     dev = device()
-    label = label or f"M={M} N={N} K={K} r={r} p={p}" + (" W=0" if zero_w else "")
+    label = label or f"M={M} N={N} K={K} r={r} p={p}" + (" W=0" if zero_w else "") + \
+        ("" if dq else " no DQ")
     print(f"[case] dropout {label}", flush=True)
     W, X, A, B, dY = synthetic.linear_inputs(M, N, K, r, dev, seed=seed)
     if zero_w:
         W = torch.zeros_like(W)
     s = alpha / r
     mask = q.qlora_dropout_mask(M, K, p, seed + 101, 5, device=dev)
-    st = q.qlora_nf4_quantize(W)
+    st = q.qlora_nf4_quantize(W, double_quant=dq)
     Y, T = q.qlora_linear_fwd_dropout(X, st, A, B, s, mask, p)
     dX, dA, dB = q.qlora_linear_bwd_dropout(dY, X, T if T_given else None, st, A, B, s, mask, p)
     torch.cuda.synchronize()
     keep = oracle.dropout_keep(M, K, p, seed + 101, 5)
     assert np.array_equal(_mask_np(mask), oracle.pack_keep(keep)), label + " mask"
     ks = oracle.keep_scale(p)
-    _, wp = oracle_wprime(W)
+    if dq:
+        _, wp = oracle_wprime(W)
+    else:
+        ref = oracle.quantize(host_f32(W).ravel())
+        wp = oracle.dequantize_nodq(ref["codes"], ref["absmax"], N * K).reshape(N, K)
     Xh, Ah, Bh, dYh = host_f32(X), host_f32(A), host_f32(B), host_f32(dY)
     Yo, To = oracle.linear_fwd(Xh, wp, Ah, Bh, s, keep=keep, keep_scale=ks)
     dXo, dAo, dBo = oracle.linear_bwd(dYh, Xh, wp, Ah, Bh, s, keep=keep, keep_scale=ks)
@@ -112,6 +117,12 @@ def test_dropout_parity_zero_weight(q, shape):
     """W = 0: Y = s D(X) A B and dX = s ((G A^T) o keep) f, nothing else."""
     M, N, K, r = shape
     _run(q, M, N, K, r, 2 * r, 0.3, seed=M + 2 * N + K, zero_w=True)
+
+
+@pytest.mark.parametrize("shape", [(300, 320, 192, 16), (16, 256, 256, 8)])
+def test_dropout_on_store_without_double_quant(q, shape):
+    M, N, K, r = shape
+    _run(q, M, N, K, r, 2 * r, 0.1, seed=M + N, dq=False)
 
 
 def test_p_zero_matches_plain_path(q):
