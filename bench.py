@@ -47,12 +47,17 @@ PMC_SHAPE = dict(M=2048, N=11008, K=4096, r=64, alpha=16)
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank space removed, so
+    that an edit of a comment leaves stored counter data valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bit_quantized_finetuning_quantize_amd", "csrc", f),
-                  "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_quantized_finetuning_quantize_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
