@@ -6,7 +6,7 @@ What is computed, and where the pages say so:
   so that each bin carries the same probability mass, then scaled into
   [-1, 1] ([P2] "How It Works" item 1; [P4] "How it works / Why NormalFloat";
   [P5] "Three refinements that keep the intelligence intact").
-  Readings where the pages are silent (each listed in the design doc):
+  Readings where the pages are silent:
   the type keeps an exact zero and both endpoints -1 and +1, which forces an
   asymmetric split (7 negative levels, 0, 8 positive levels, equal mass per
   bin within each half); the inverse CDF at 1 is infinite, so the outermost
