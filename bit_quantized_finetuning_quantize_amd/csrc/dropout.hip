@@ -2,8 +2,9 @@
 //
 // ozercemkelahmet.com "QLoRA": the LoraConfig of "A code example with common
 // libraries" trains with a LoRA dropout of 0.05, and "Practical guidance and
-// best practices", Adapter settings, adds light dropout for small datasets. Each element of the [M x K] adapter
-// input is kept independently with probability 1 - thr / 2^16.
+// best practices", Adapter settings, recommends a small dropout rate when
+// the training data is scarce. Each element of the [M x K] adapter input is
+// kept independently with probability 1 - thr / 2^16.
 //
 // Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
 // random numbers: as easy as 1, 2, 3", SC'11): key = the 64-bit seed, counter

@@ -168,8 +168,8 @@ int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* 
 
 /* qlora_adamw_step — one AdamW step for adapter parameters, in place
  * (ozercemkelahmet.com "QLoRA", "Practical guidance and best practices",
- * Optimizer and schedule: a paged 8-bit or 32-bit AdamW; same page, "How it
- * works", Step 7). Float32 parameters p, moments m and v, gradient g (for
+ * Optimizer and schedule: AdamW with paged state in 8 or 32 bits; same
+ * page, "How it works", Step 7). Float32 parameters p, moments m and v, gradient g (for
  * example dA or dB of qlora_linear_bwd), n elements each; step t >= 1 counts
  * from 1. Each operation is one float32 operation rounded on its own, in
  * this order (host constants computed in float64 and rounded once):
@@ -306,7 +306,8 @@ int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X,
  * Dropout on the input of the adapter path only (ozercemkelahmet.com
  * "QLoRA": the LoraConfig of "A code example with common libraries" trains
  * with lora_dropout = 0.05; "Practical guidance and best practices", Adapter
- * settings: light dropout for small datasets). With a keep mask over X and f the inverse keep probability,
+ * settings: a small dropout rate when data is scarce). With a keep mask over
+ * X and f the inverse keep probability,
  *   D(X) = (X o keep) f,   Y = X bf16(W')^T + scale * (D(X) A) B,
  * the frozen-weight product sees X unchanged (inverted dropout).
  *

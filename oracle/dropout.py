@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY.
 
 The pages' training recipe sets a LoRA dropout of 0.05 ([P4] "A code example
 with common libraries", its LoraConfig; "Practical guidance and best
-practices", Adapter settings: light dropout for small datasets). Reading taken here: inverted
-dropout on the input of the adapter path only, the frozen-weight product
-sees X unchanged:
+practices", Adapter settings: a small dropout rate when data is scarce).
+Reading taken here: inverted dropout on the input of the adapter path only,
+the frozen-weight product sees X unchanged:
 
     D(X) = (X o keep) * keep_scale,      Y = X W'^T + s D(X) A B
 

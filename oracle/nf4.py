@@ -37,7 +37,7 @@ What is computed, and where the pages say so:
   by q8 = 255 at the group maximum and by the half-step error bound.
 
 * Without double quantization ([P4] "Step 2: store the scale per block": a
-  32-bit constant per block of 64, half a bit per weight) the store keeps
+  32-bit constant per block of 64, i.e. 0.5 bits per weight) the store keeps
   each block's float32 constant c itself, and w' = fl32(L4[q] * c); the
   level-1 codes are the same as with double quantization. Pinned by the
   worked example's printed values, an exact rational recomputation of
