@@ -12,7 +12,8 @@
     apart), T recomputed in the backward gives the same gradients bit for
     bit, the rank limit of the masked input gradient;
   * the full-size prefill projections (gate 11008x4096 in full, down
-    4096x11008 on sampled rows).
+    4096x11008 on sampled rows) and the 65B-shaped down projection
+    (8192x22016, 4096 tokens) on sampled rows.
 """
 
 import numpy as np
@@ -217,3 +218,34 @@ def test_prefill_down_sampled(q):
                                     keep_scale=ks)
     assert_close(host_f32(dA), dAo, "down dA")
     assert_close(host_f32(dB), dBo, "down dB")
+
+
+def test_stress_down_projection_sampled(q):
+    """The 65B-shaped down projection (W 8192x22016, Student-t weights),
+    4096 tokens, p = 0.05: the mask in full, T, Y and dX on sampled rows,
+    dA and dB in full."""
+    dev = device()
+    M, N, K, r, s, p = 4096, 8192, 22016, 64, 16 / 64, 0.05
+    print("[case] dropout stress down 8192x22016 M=4096", flush=True)
+    W, X, A, B, dY = synthetic.linear_inputs(M, N, K, r, dev, seed=2, weight="student_t")
+    st = q.qlora_nf4_quantize(W)
+    mask = q.qlora_dropout_mask(M, K, p, 5150, 11, device=dev)
+    Y, T = q.qlora_linear_fwd_dropout(X, st, A, B, s, mask, p)
+    dX, dA, dB = q.qlora_linear_bwd_dropout(dY, X, T, st, A, B, s, mask, p)
+    torch.cuda.synchronize()
+    keep = oracle.dropout_keep(M, K, p, 5150, 11)
+    assert np.array_equal(_mask_np(mask), oracle.pack_keep(keep))
+    ks = oracle.keep_scale(p)
+    rows = np.sort(np.random.default_rng(2).choice(M, 24, replace=False))
+    _, wp = oracle_wprime(W)
+    Xh, Ah, Bh, dYh = host_f32(X), host_f32(A), host_f32(B), host_f32(dY)
+    Yo, To = oracle.linear_fwd(Xh[rows], wp, Ah, Bh, s, keep=keep[rows], keep_scale=ks)
+    assert_close(host_f32(T)[rows], To, "stress down T rows", tol=1e-5)
+    assert_close(host_f32(Y)[rows], Yo, "stress down Y rows")
+    dXo, _, _ = oracle.linear_bwd(dYh[rows], Xh[rows], wp, Ah, Bh, s, keep=keep[rows],
+                                  keep_scale=ks)
+    assert_close(host_f32(dX)[rows], dXo, "stress down dX rows")
+    _, dAo, dBo = oracle.linear_bwd(dYh, Xh, np.zeros((N, K), np.float32), Ah, Bh, s, keep=keep,
+                                    keep_scale=ks)
+    assert_close(host_f32(dA), dAo, "stress down dA")
+    assert_close(host_f32(dB), dBo, "stress down dB")
