@@ -48,6 +48,7 @@ constexpr int threads_for() { return cons_waves<PT, LB>() * 64 + kProducerThread
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 // byte offset of logical 16-byte chunk c of tile row `row`
@@ -444,9 +445,11 @@ struct LoadNone {
 // ---------------------------------------------------------------------------
 // Epilogues
 
-// bf16 output, row-major [P x Q] with leading dimension ld.
+// bf16 output, row-major [P x Q] with leading dimension ld. Written
+// through LDS in whole row segments (Consumer::store_bf16_staged).
 struct EpiBf16 {
   static constexpr bool kKeepSeg2 = false;
+  static constexpr bool kStaged = true;
   uint16_t* out;
   int64_t ld, P, Q;
   __device__ __forceinline__ void put(int64_t p, int64_t q, float v) const {
@@ -460,6 +463,7 @@ struct EpiBf16 {
 // its kept elements (at most three second-segment steps, one split).
 struct EpiBf16Keep {
   static constexpr bool kKeepSeg2 = true;
+  static constexpr bool kStaged = false;
   uint16_t* out;
   int64_t ld, P, Q;
   const uint32_t* mask;
@@ -472,6 +476,7 @@ struct EpiBf16Keep {
 // float32 split-K partial: out[split][p][q], dense [P x Q] per split.
 struct EpiPartial {
   static constexpr bool kKeepSeg2 = false;
+  static constexpr bool kStaged = false;
   float* out;
   int64_t P, Q;
   __device__ __forceinline__ void put(int64_t p, int64_t q, float v, int split) const {
@@ -609,6 +614,56 @@ struct Consumer {
     }
   }
 
+  // bf16 row-major output through a per-wave LDS staging area at `buf`
+  // (32 rows at kStagePitch bytes per wave): each 32-row block of the wave's
+  // tile is written to LDS as bf16, read back as 16-byte row chunks and
+  // stored as whole 128-byte row segments, 8 global stores per block where
+  // element stores would take 64. Rows whose stride, alignment or edge does
+  // not allow a 16-byte store take 2-byte stores. The values are those of
+  // the element-wise epilogue, bit for bit.
+  static constexpr int kStagePitch = WQ * 2 + 16;  // 16 bytes of padding per row
+  __device__ __forceinline__ void store_bf16_staged(uint16_t* out, int64_t ld, int64_t P,
+                                                    int64_t Q, int64_t p0, int64_t q0,
+                                                    uint32_t buf, int wave, int lane) const {
+    static_assert(WQ == 64, "eight 16-byte chunks per staged row");
+    const int wp = wave >> 1, wq = wave & 1;
+    const uint32_t wb = buf + (uint32_t)(wave * 32 * kStagePitch);
+    const bool vec = (ld & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < BP; ++i) {
+      // elements v and v + 1 of a block are rows r and r + 1 of one column
+#pragma unroll
+      for (int j = 0; j < BQ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const uint32_t pk = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
+          const int r = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const uint32_t a = wb + (uint32_t)(r * kStagePitch + (j * 32 + (lane & 31)) * 2);
+          *(lds_u16*)(uintptr_t)a = (uint16_t)(pk & 0xffffu);
+          *(lds_u16*)(uintptr_t)(a + kStagePitch) = (uint16_t)(pk >> 16);
+        }
+      // the wave's LDS accesses complete in order: these reads see the
+      // writes above, and the next block's writes come after them
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = k * 8 + (lane >> 3), ch = lane & 7;
+        const u32x4 d =
+            *(const lds_u32x4*)(uintptr_t)(wb + (uint32_t)(row * kStagePitch + ch * 16));
+        const int64_t p = p0 + wp * WP + i * 32 + row;
+        const int64_t q = q0 + wq * WQ + ch * 8;
+        if (p >= P) continue;
+        uint16_t* o = out + p * ld + q;
+        if (vec && q + 8 <= Q) {
+          *(u32x4*)o = d;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (q + e < Q) o[e] = (uint16_t)(d[e >> 1] >> ((e & 1) * 16));
+        }
+      }
+    }
+  }
+
   // Visit every accumulator element with its (p, q) tile coordinates.
   template <class F>
   __device__ __forceinline__ void for_each(int wave, int lane, F&& f) const {
@@ -740,6 +795,18 @@ __device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, 
     }
     if constexpr (kPartial) {
       cons.for_each(wave, lane, [&](int p, int q, float v) { cfg.epi.put(p0 + p, q0 + q, v, split); });
+    } else if constexpr (Epi::kStaged) {
+      // Stage (n+1) % 3 is free once this wave has passed the last barrier
+      // (#n-1): every consumer finished reading it (step n-2) before that
+      // barrier, and no load writes it afterwards. The only loads that can
+      // still be landing are the first segment's past-the-end direct loads,
+      // and they fill stage n1 % 3, which is n % 3 without a second segment
+      // and is waited for by the producers before it with one. The other
+      // consumers may still be reading stage (n-1) % 3.
+      static_assert(kCW * 32 * Consumer<PT, QT, kCW>::kStagePitch <= kStageBytes,
+                    "staging area inside one stage");
+      cons.store_bf16_staged(cfg.epi.out, cfg.epi.ld, cfg.epi.P, cfg.epi.Q, p0, q0, stage(n + 1),
+                             wave, lane);
     } else {
       cons.for_each(wave, lane, [&](int p, int q, float v) { cfg.epi.put(p0 + p, q0 + q, v); });
     }
