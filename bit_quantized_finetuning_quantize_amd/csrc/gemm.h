@@ -843,13 +843,16 @@ __device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, 
       if constexpr (!kConsA) a1.direct(g, sa, t);
     };
 
-    // prologue: step 0 complete in stage 0; direct loads of step 1; regs 1, 2
+    // prologue: step 0 complete in stage 0; direct loads of step 1; regs 1, 2.
+    // Step 1's loads are issued before the wait for step 0, so that the two
+    // travel together; loads complete in issue order, so waiting until the
+    // newest kDir + kReg are the only ones outstanding covers step 0.
     a1_direct(g0, stage(0)); b1.direct(g0, stage(0) + kBOff, t);
     a1.load(g0, ra0, t); b1.load(g0, rb0, t);
-    wait_vmcnt<0>();
-    a1.store(ra0, stage(0), tb, t); b1.store(rb0, stage(0) + kBOff, tb, t);
     a1_direct(g0 + 1, stage(1)); b1.direct(g0 + 1, stage(1) + kBOff, t);
     a1.load(g0 + 1, ra1, t); b1.load(g0 + 1, rb1, t);
+    wait_vmcnt<kDir + kReg>();
+    a1.store(ra0, stage(0), tb, t); b1.store(rb0, stage(0) + kBOff, tb, t);
     a1.load(g0 + 2, ra0, t); b1.load(g0 + 2, rb0, t);
     stage_barrier();  // barrier #0: step 0 ready
 
