@@ -45,9 +45,11 @@ __device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g,
   v = v1;
 }
 
-// Four parameters per thread and 16-byte accesses where the arrays allow it
-// (n % 4 == 0 and 16-byte aligned pointers); one parameter per thread
-// otherwise.
+// 16-byte accesses where the arrays allow it (n % 4 == 0 and 16-byte aligned
+// pointers): two units of four parameters per thread, all eight loads issued
+// before any arithmetic, non-temporal (every byte is read and written once
+// per step), with a grid large enough that each thread has only its own two
+// units; one parameter per thread otherwise.
 template <bool kVec>
 __global__ void __launch_bounds__(256)
 adamw_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
@@ -55,22 +57,36 @@ adamw_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v
              uint16_t* __restrict__ p16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (kVec) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n / 4; i += stride) {
-      floatx4 pp = reinterpret_cast<floatx4*>(p)[i];
-      floatx4 mm = reinterpret_cast<floatx4*>(m)[i];
-      floatx4 vv = reinterpret_cast<floatx4*>(v)[i];
-      const floatx4 gg = reinterpret_cast<const floatx4*>(g)[i];
+    const int64_t units = n / 4;
+    for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i0 < units; i0 += 2 * stride) {
+      floatx4 pp[2], mm[2], vv[2], gg[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float a = pp[c], b = mm[c], d = vv[c];
-        adamw_one(a, b, d, gg[c], k);
-        pp[c] = a; mm[c] = b; vv[c] = d;
+      for (int u = 0; u < 2; ++u) {
+        const int64_t i = i0 + u * stride;
+        if (i >= units) break;
+        pp[u] = __builtin_nontemporal_load(&reinterpret_cast<floatx4*>(p)[i]);
+        mm[u] = __builtin_nontemporal_load(&reinterpret_cast<floatx4*>(m)[i]);
+        vv[u] = __builtin_nontemporal_load(&reinterpret_cast<floatx4*>(v)[i]);
+        gg[u] = __builtin_nontemporal_load(&reinterpret_cast<const floatx4*>(g)[i]);
       }
-      reinterpret_cast<floatx4*>(p)[i] = pp;
-      reinterpret_cast<floatx4*>(m)[i] = mm;
-      reinterpret_cast<floatx4*>(v)[i] = vv;
-      if (p16)
-        reinterpret_cast<u32x2*>(p16)[i] = u32x2{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3])};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t i = i0 + u * stride;
+        if (i >= units) break;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float a = pp[u][c], b = mm[u][c], d = vv[u][c];
+          adamw_one(a, b, d, gg[u][c], k);
+          pp[u][c] = a; mm[u][c] = b; vv[u][c] = d;
+        }
+        __builtin_nontemporal_store(pp[u], &reinterpret_cast<floatx4*>(p)[i]);
+        __builtin_nontemporal_store(mm[u], &reinterpret_cast<floatx4*>(m)[i]);
+        __builtin_nontemporal_store(vv[u], &reinterpret_cast<floatx4*>(v)[i]);
+        if (p16) {
+          const u32x2 b16 = u32x2{pack_bf16x2(pp[u][0], pp[u][1]), pack_bf16x2(pp[u][2], pp[u][3])};
+          __builtin_nontemporal_store(b16, &reinterpret_cast<u32x2*>(p16)[i]);
+        }
+      }
     }
   } else {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -90,7 +106,8 @@ adamw_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v
 //   code = enc(fl(x / scale)) (0 when scale = 0), top = 448 / 57344,
 // enc rounding to nearest, ties to the even code, saturating at top. One
 // wave owns one block: four parameters per lane, the block maxima by a
-// wave-wide reduction.
+// wave-wide reduction. The parameter, gradient and code accesses are
+// non-temporal: each byte is read and written once per step.
 
 // dec: the value of a code, exactly (the exponent field goes straight into
 // the float's exponent; subnormals are m 2^(1 - bias - mbits)).
@@ -152,12 +169,12 @@ adamw8_kernel(float* __restrict__ p, uint8_t* __restrict__ m8, float* __restrict
     uint32_t mc = 0, vc = 0;
     const bool whole = e0 + 4 <= n;
     if (kVec && whole) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(p + e0);
-      const floatx4 c = *reinterpret_cast<const floatx4*>(g + e0);
+      const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + e0));
+      const floatx4 c = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + e0));
 #pragma unroll
       for (int j = 0; j < 4; ++j) { pv[j] = a[j]; gv[j] = c[j]; }
-      mc = *reinterpret_cast<const uint32_t*>(m8 + e0);
-      vc = *reinterpret_cast<const uint32_t*>(v8 + e0);
+      mc = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(m8 + e0));
+      vc = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(v8 + e0));
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -202,11 +219,11 @@ adamw8_kernel(float* __restrict__ p, uint8_t* __restrict__ m8, float* __restrict
       vo |= cv << (8 * j);
     }
     if (kVec && whole) {
-      *reinterpret_cast<floatx4*>(p + e0) = floatx4{pv[0], pv[1], pv[2], pv[3]};
-      *reinterpret_cast<uint32_t*>(m8 + e0) = mo;
-      *reinterpret_cast<uint32_t*>(v8 + e0) = vo;
+      __builtin_nontemporal_store(floatx4{pv[0], pv[1], pv[2], pv[3]}, reinterpret_cast<floatx4*>(p + e0));
+      __builtin_nontemporal_store(mo, reinterpret_cast<uint32_t*>(m8 + e0));
+      __builtin_nontemporal_store(vo, reinterpret_cast<uint32_t*>(v8 + e0));
       if (p16)
-        *reinterpret_cast<u32x2*>(p16 + e0) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        __builtin_nontemporal_store(u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])}, reinterpret_cast<u32x2*>(p16 + e0));
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -249,8 +266,9 @@ hipError_t launch_adamw8(float* p, uint8_t* m8, float* sm, uint8_t* v8, float* s
                    ((reinterpret_cast<uintptr_t>(m8) | reinterpret_cast<uintptr_t>(v8)) & 3) == 0 &&
                    (reinterpret_cast<uintptr_t>(p16) & 7) == 0;
   const int64_t nb = (n + kBlock8 - 1) / kBlock8;
+  // one wave per block of 256 parameters; a capped grid strides over the rest
   int64_t blocks = (nb + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > ((int64_t)1 << 30)) blocks = (int64_t)1 << 30;
   if (blocks < 1) blocks = 1;
   if (vec)
     hipLaunchKernelGGL(adamw8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, m8, sm,
@@ -270,8 +288,9 @@ hipError_t launch_adamw(float* p, float* m, float* v, const float* g, int64_t n,
                                   15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p16) & 7) == 0;
   const int64_t units = vec ? n / 4 : n;
-  int64_t blocks = (units + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
+  // two units per thread; a capped grid strides over the rest
+  int64_t blocks = (units + 511) / 512;
+  if (blocks > ((int64_t)1 << 30)) blocks = (int64_t)1 << 30;
   if (blocks < 1) blocks = 1;
   if (vec)
     hipLaunchKernelGGL(adamw_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, m, v, g,
