@@ -28,7 +28,9 @@ def _np(t):
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("n,shift", [(4096, 0), (1001, 0), (4097, 1), (64 * 3, 3)])
+# 2800: 700 four-parameter units on a 512-thread grid, so that some threads
+# of the vectorized path have a second unit and the others do not
+@pytest.mark.parametrize("n,shift", [(4096, 0), (2800, 0), (1001, 0), (4097, 1), (64 * 3, 3)])
 def test_adamw_bit_exact_over_steps(q, n, shift):
     print(f"[case] adamw n={n} shift={shift}", flush=True)
     dev = device()
