@@ -121,6 +121,35 @@ def test_deterministic_and_T_recompute(q):
         assert torch.equal(a, b)
 
 
+def test_outputs_at_two_byte_offsets(q):
+    """Y and dX written at a 2-byte offset (allowed: the outputs need only
+    2-byte alignment): the contraction kernels then store their bf16 tiles
+    element by element instead of in 16-byte row chunks. The values must be
+    those of the aligned call, bit for bit, with nothing written outside
+    the outputs."""
+    dev = device()
+    M, N, K, r = 300, 320, 192, 16
+    print(f"[case] unaligned outputs M={M} N={N} K={K} r={r}", flush=True)
+    W, X, A, B, dY = synthetic.linear_inputs(M, N, K, r, dev, seed=21)
+    st = q.qlora_nf4_quantize(W)
+    Y1, T1 = q.qlora_linear_fwd(X, st, A, B, 0.5)
+    dX1, dA1, dB1 = q.qlora_linear_bwd(dY, X, T1, st, A, B, 0.5)
+    sentinel = -7
+    ybuf = torch.full((M * N + 2,), sentinel, dtype=torch.int16, device=dev)
+    xbuf = torch.full((M * K + 2,), sentinel, dtype=torch.int16, device=dev)
+    Y2 = ybuf[1:1 + M * N].view(torch.bfloat16).view(M, N)
+    dX2 = xbuf[1:1 + M * K].view(torch.bfloat16).view(M, K)
+    assert Y2.data_ptr() % 16 != 0 and dX2.data_ptr() % 16 != 0
+    _, T2 = q.qlora_linear_fwd(X, st, A, B, 0.5, Y=Y2)
+    _, dA2, dB2 = q.qlora_linear_bwd(dY, X, T2, st, A, B, 0.5, dX=dX2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    assert torch.equal(dX1.view(torch.int16), dX2.view(torch.int16))
+    assert torch.equal(T1, T2) and torch.equal(dA1, dA2) and torch.equal(dB1, dB2)
+    for buf, n in ((ybuf, M * N), (xbuf, M * K)):
+        assert buf[0].item() == sentinel and buf[n + 1].item() == sentinel
+
+
 def test_prefill_projection_full(q):
     """One full-size projection of the prefill MLP workload:
     gate W 11008x4096, X 2048x4096, r=64, alpha=16, compared in full."""
