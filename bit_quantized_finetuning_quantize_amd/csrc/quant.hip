@@ -5,9 +5,9 @@
 // Quantization follows ozercemkelahmet.com "QLoRA", How it works, Step 1
 // (blocks of 64 scaled by their largest magnitude, each value replaced by
 // the nearest of 16 NormalFloat levels), Step 2 (one constant per block) and
-// Step 3 (the constants quantized again to 8 bits in groups with their own
-// second-level constants); ai360xpert.com "QLoRA", How It Works item 2
-// (32-bit constants to 8-bit).
+// Step 3 (block maxima stored as 8-bit fractions of one float32 maximum per
+// group of 256 blocks); ai360xpert.com "QLoRA", How It Works item 2 (the
+// per-block constants shrink from 32 to 8 bits).
 //
 // Layout of one launch: one workgroup per group of 256 blocks (16384 values).
 // Within a workgroup, eight consecutive lanes own one block (8 values each,

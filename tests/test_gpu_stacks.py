@@ -13,9 +13,10 @@ The oracle runs on samples it can compute exactly: a flat span that starts
 on a 16384-value group boundary quantizes independently of the rest of the
 tensor, so the stores are compared byte for byte on such spans, and Y on
 sampled token rows times sampled output features (the weight rows, each
-quantized inside its group-aligned span). dX is compared in full-oracle
-form on one whole linear; dA and dB, which do not involve the weight, on
-sampled rows."""
+quantized inside its group-aligned span). dX, which every output feature
+enters, is compared on sampled token rows against the oracle's store of the
+whole weight; dA and dB, which do not involve the weight, on sampled rows
+and columns, each through oracle.linear_bwd."""
 
 import json
 import os
@@ -90,28 +91,60 @@ def _check_y_sampled(Y, X, W, A, B, s, label, n_rows=16, n_cols=24, seed=0):
 
 
 def _check_lora_grads_sampled(dA, dB, dY, X, A, B, s, label, n=32, seed=1):
-    """dA = s X^T G and dB = s T^T dY (G = dY B^T, T = X A) on sampled rows
-    of dA and sampled columns of dB; the weight does not enter."""
+    """dA on sampled rows and dB on sampled columns against oracle.linear_bwd.
+    Neither gradient involves the frozen weight, so the oracle is called on
+    the sampled slice with a zero weight of the matching shape: dA[kr] =
+    s X[:, kr]^T G needs the full G = dY B^T and only the sampled columns of
+    X (and rows of A), dB[:, nc] = s T^T dY[:, nc] needs the full T = X A
+    and only the sampled columns of dY (and of B)."""
     K, r = dA.shape
     N = dB.shape[1]
     rng = np.random.default_rng(seed)
     kr = np.sort(rng.choice(K, n, replace=False))
     nc = np.sort(rng.choice(N, n, replace=False))
-    Xh = host_f32(X).astype(np.float64)
-    dYh = host_f32(dY).astype(np.float64)
-    Ah = host_f32(A).astype(np.float64)
-    Bh = host_f32(B).astype(np.float64)
-    G = dYh @ Bh.T
-    T = Xh @ Ah
-    dAo = s * (Xh[:, kr].T @ G)
-    dBo = s * (T.T @ dYh[:, nc])
+    Xh, dYh, Ah, Bh = host_f32(X), host_f32(dY), host_f32(A), host_f32(B)
+    _, dAo, _ = oracle.linear_bwd(dYh, Xh[:, kr], np.zeros((N, n), np.float32), Ah[kr], Bh, s)
+    _, _, dBo = oracle.linear_bwd(dYh[:, nc], Xh, np.zeros((n, K), np.float32), Ah, Bh[:, nc], s)
     assert_close(host_f32(dA)[kr], dAo, f"{label} dA rows")
     assert_close(host_f32(dB)[:, nc], dBo, f"{label} dB columns")
 
 
+def _oracle_wprime_parallel(W, parts=16):
+    """The oracle's float32 w' of a whole weight: oracle.quantize and
+    oracle.dequantize on group-aligned flat spans (which quantize
+    independently of the rest of the tensor), run on a thread pool (numpy
+    releases the interpreter lock inside its array operations)."""
+    from concurrent.futures import ThreadPoolExecutor
+    N, K = W.shape
+    flat = host_f32(W).ravel()
+    numel = flat.size
+    ngroups = -(-numel // SPAN)
+    bounds = sorted({min(numel, (ngroups * i // parts) * SPAN) for i in range(parts + 1)})
+
+    def one(span):
+        g0, g1 = span
+        ref = oracle.quantize(flat[g0:g1])
+        return oracle.dequantize(ref["codes"], ref["absmax_q"], ref["absmax_s2"], g1 - g0)
+
+    with ThreadPoolExecutor(max_workers=min(parts, os.cpu_count() or 1)) as ex:
+        pieces = list(ex.map(one, zip(bounds[:-1], bounds[1:])))
+    return np.concatenate(pieces).reshape(N, K)
+
+
+def _check_dx_sampled(dX, dY, X, W, A, B, s, label, n_rows=16, seed=5):
+    """dX on sampled token rows against oracle.linear_bwd with the oracle's
+    own store of the whole weight (every output feature enters each row)."""
+    M = dX.shape[0]
+    wp = _oracle_wprime_parallel(W)
+    rows = np.sort(np.random.default_rng(seed).choice(M, n_rows, replace=False))
+    dXo, _, _ = oracle.linear_bwd(host_f32(dY)[rows], host_f32(X)[rows], wp, host_f32(A),
+                                  host_f32(B), s)
+    assert_close(host_f32(dX)[rows], dXo, f"{label} dX rows")
+
+
 def test_stack_7b_full_sweep(q):
     """Every linear of the 32-layer stack, forward and backward at 2048
-    tokens; stores, Y and the adapter gradients checked on samples of three
+    tokens; stores, Y, dX and the adapter gradients checked on samples of three
     linears spread over the stack, every output checked to be finite."""
     dev = device()
     M, r, alpha = 2048, 64, 16
@@ -137,6 +170,7 @@ def test_stack_7b_full_sweep(q):
                 for g0 in (0, (N * K // SPAN // 2) * SPAN):
                     _check_store_span(st, W, g0, min(N * K, g0 + 4 * SPAN), label)
                 _check_y_sampled(Y, X, W, A, B, s, label)
+                _check_dx_sampled(dX, dY, X, W, A, B, s, label, seed=layer)
                 _check_lora_grads_sampled(dA, dB, dY, X, A, B, s, label)
             del W, X, A, B, dY, st, Y, T, dX, dA, dB
     # the store sizes of the oracle's layout (3,340,771,328 bytes, pinned by
@@ -181,9 +215,10 @@ def test_stress_65b_quantize_all(q):
 
 def test_stress_65b_one_layer(q):
     """Layer 0 of the 65B-shaped stack, forward and backward at 4096 tokens:
-    Y on sampled rows x features for every linear, dX against the full
-    oracle on the q projection (sampled token rows), dA and dB on samples
-    for q and down."""
+    Y on sampled rows x features, dX on sampled token rows against the oracle's
+    whole dequantized weight, dA and dB on sampled rows and columns, for
+    every linear (gate and up contract over N = 22016 in dX, down writes
+    K = 22016)."""
     dev = device()
     M, r, alpha = 4096, 64, 16
     s = alpha / r
@@ -201,14 +236,6 @@ def test_stress_65b_one_layer(q):
         for name, t in (("Y", Y), ("dX", dX), ("dA", dA), ("dB", dB)):
             assert bool(torch.isfinite(t).all()), f"{label}: non-finite {name}"
         _check_y_sampled(Y, X, W, A, B, s, label, seed=j)
-        if j == 0:
-            ref = oracle.quantize(host_f32(W).ravel())
-            wp = oracle.dequantize(ref["codes"], ref["absmax_q"], ref["absmax_s2"],
-                                   N * K).reshape(N, K)
-            rows = np.sort(np.random.default_rng(5).choice(M, 16, replace=False))
-            dXo, _, _ = oracle.linear_bwd(host_f32(dY)[rows], host_f32(X)[rows], wp,
-                                          host_f32(A), host_f32(B), s)
-            assert_close(host_f32(dX)[rows], dXo, f"{label} dX rows")
-        if j in (0, 6):
-            _check_lora_grads_sampled(dA, dB, dY, X, A, B, s, label)
+        _check_dx_sampled(dX, dY, X, W, A, B, s, label, seed=5 + j)
+        _check_lora_grads_sampled(dA, dB, dY, X, A, B, s, label, seed=j)
         del W, X, A, B, dY, st, Y, T, dX, dA, dB
