@@ -517,7 +517,7 @@ def run_gemv(args, q, synthetic, torch, dev):
                             roofline={"bound": "hbm", "achieved": round(gbps, 1),
                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                       "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                                      "per": "call (main + epilogue launch)"})
+                                      "per": "call (T partials launch + fused GEMV launch)"})
         log(f"[gemv] M={M}: {call_us:.2f} us/call, {gbps:.0f} GB/s effective weight")
     # context for the per-call figures: one vectorized torch elementwise
     # launch that reads the same number of bytes (an int64 view, compared

@@ -170,6 +170,29 @@ __device__ __forceinline__ u32x4 dequant_word_perm(uint32_t w, const PermTable& 
                __builtin_amdgcn_perm(zv23, xy23, 0x07060302u)};
 }
 
+// The same lookups with the elements left in the order 0, 2, 4, 6, 1, 3, 5, 7
+// (word 0 holds elements 0 and 2, word 1 elements 4 and 6, word 2 elements
+// 1 and 3, word 3 elements 5 and 7): one byte interleave per output word
+// instead of two. A contraction that takes its other operand in the same
+// order (x_order_oddeven) sums the same products.
+__device__ __forceinline__ u32x4 dequant_word_perm_oddeven(uint32_t w, const PermTable& t) {
+  const uint32_t m_lo = __builtin_amdgcn_perm(w << 4, w << 12, 0x0B090A08u);
+  const uint32_t m_hi = __builtin_amdgcn_perm(w, w << 8, 0x0B090A08u);
+  const uint32_t s_lo = w & 0x07070707u, s_hi = (w >> 4) & 0x07070707u;
+  const uint32_t xl = perm_lookup(t.lo, s_lo, m_lo);  // low bytes, even elements
+  const uint32_t xh = perm_lookup(t.hi, s_lo, m_lo);  // high bytes, even elements
+  const uint32_t zl = perm_lookup(t.lo, s_hi, m_hi);  // low bytes, odd elements
+  const uint32_t zh = perm_lookup(t.hi, s_hi, m_hi);  // high bytes, odd elements
+  return u32x4{__builtin_amdgcn_perm(xh, xl, 0x05010400u), __builtin_amdgcn_perm(xh, xl, 0x07030602u),
+               __builtin_amdgcn_perm(zh, zl, 0x05010400u), __builtin_amdgcn_perm(zh, zl, 0x07030602u)};
+}
+// Eight consecutive bf16 values (word j holds elements 2j, 2j + 1) put in
+// the element order of dequant_word_perm_oddeven.
+__device__ __forceinline__ u32x4 x_order_oddeven(const u32x4& v) {
+  return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+               __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+}
+
 // 8 codes -> 4 words of bf16 pairs bf16(fl32(L[q] * cs)): two roundings,
 // never fused.
 __device__ __forceinline__ u32x4 dequant_word8(uint32_t word, float cs, const float* lv,

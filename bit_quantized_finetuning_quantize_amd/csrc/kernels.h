@@ -62,7 +62,8 @@ struct Dropout {
 // Workspace carve-up for the forward and backward of one linear call.
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
-// Small-M forward (M <= kGemvMaxM): split-K GEMV with the LoRA epilogue.
+// Small-M forward (M <= kGemvMaxM): split partials of T = X A, then one
+// GEMV launch over row tiles of the whole K that adds s T B and writes Y.
 constexpr int kGemvMaxM = 16;
 int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A,

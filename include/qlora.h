@@ -36,7 +36,7 @@
  * - Calls that share a workspace buffer must not overlap in time (same
  *   stream, or caller-side ordering). Otherwise calls are thread-safe: host
  *   threads may call concurrently on their own streams with their own
- *   buffers (the only process state is a per-device flag, set once under an
+ *   buffers (the only process state is per-device flags, set once under an
  *   atomic, recording that a kernel's LDS limit has been raised).
  *
  * The NF4 store
@@ -238,8 +238,9 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  *   T_out    device float [M x r]  optional output: T = X A (for the
  *                                  backward); NULL to skip
  * Products of bf16 values accumulate in float32. M <= 16 takes a
- * memory-bound split-K GEMV path (two launches); larger M takes an MFMA
- * GEMM path. Calls capture into a HIP graph (no memset, no allocation).
+ * memory-bound GEMV path (two launches: split partials of X A, then one
+ * kernel per 16 weight rows over the whole K that adds the adapter term and
+ * writes Y); larger M takes an MFMA GEMM path. Calls capture into a HIP graph (no memset, no allocation).
  * Errors: INVALID_ARG (null X/codes/absmax/A/B/Y, non-positive M, N, K);
  * UNSUPPORTED (K or N not a multiple of 64, r outside [1, 256], M above
  * 2^30, N or K above 2^21, M N or M K at or above 2^30, N K at or above

@@ -64,6 +64,15 @@ def test_decode_gemv_4096(q, M):
     _run(q, M, 4096, 4096, 16, 32, bwd=False, label=f"decode 4096^2 M={M} r=16")
 
 
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_gemv_down_projection(q, M):
+    """The GEMV on the 4096x11008 down projection: K = 11008 spans three
+    4096-wide passes (the last one partial, ending inside a wave's range),
+    and K / 64 = 172 blocks per row, so rows do not start on an eight-block
+    boundary and a lane's blocks may straddle a second-level group."""
+    _run(q, M, 4096, 11008, 16, 32, bwd=False, label=f"decode 4096x11008 M={M} r=16")
+
+
 @pytest.mark.parametrize("shape", [
     (17, 256, 256, 8),        # just above the GEMV limit
     (300, 320, 192, 16),      # ragged M, N not a multiple of 128, K % 128 = 64
