@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     qlora_linear_bwd_dropout,
     qlora_linear_fwd,
     qlora_linear_fwd_dropout,
+    qlora_linear_fwd_noalloc,
     qlora_linear_workspace_bytes,
     qlora_nf4_codebook,
     qlora_nf4_codes_bytes,

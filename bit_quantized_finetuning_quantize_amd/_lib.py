@@ -46,6 +46,8 @@ SIGNATURES = {
                                   _c_f32, _vp, _vp, _vp, _c_size, _vp]),
     "qlora_linear_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
                                   _c_i32, _c_f32, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "qlora_linear_fwd_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                          _c_i32, _c_f32, _vp, _vp, _vp]),
     "qlora_linear_fwd_profiled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
                                            _c_i32, _c_f32, _vp, _vp, _vp, _c_size, _vp, _vp,
                                            _vp]),

@@ -204,6 +204,24 @@ def qlora_linear_fwd(X, W, A, B, scale, want_T=True, Y=None, T=None, ws=None, ev
     return Y, (T if want_T else None)
 
 
+def qlora_linear_fwd_noalloc(X, W, A, B, scale, want_T=True, Y=None, T=None):
+    """qlora_linear_fwd without a workspace: the library's fixed per-device
+    scratch array serves as one (calls that overlap on one GPU race)."""
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[1]
+    for t, name in ((X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, name)
+    Y = Y if Y is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    if want_T and T is None:
+        T = torch.empty(M, r, dtype=torch.float32, device=X.device)
+    _check(LIB.qlora_linear_fwd_noalloc(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q),
+                                        _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r,
+                                        float(scale), _ptr(Y), _ptr(T) if want_T else None,
+                                        _stream()))
+    return Y, (T if want_T else None)
+
+
 def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, dB=None, ws=None,
                      events=None):
     """Returns (dX or None, dA fp32 [K x r], dB fp32 [r x N]).

@@ -195,6 +195,26 @@ int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes, const uint8_t* abs
                                    T_out, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
+int qlora_linear_fwd_noalloc(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                             const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                             int64_t M, int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y,
+                             float* T_out, void* stream) {
+  static_assert(QLORA_NOALLOC_SCRATCH_BYTES == qlora::kNoAllocScratchBytes, "scratch size");
+  if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  int st = check_store(codes, absmax_q, absmax_s2);
+  if (st != QLORA_OK) return st;
+  st = check_linear_shape(M, N, K, r);
+  if (st != QLORA_OK) return st;
+  if (!aligned(X, 16) || !aligned(B, 16) || !aligned(A, 2) || !aligned(Y, 2) ||
+      (T_out && !aligned(T_out, 4)))
+    return QLORA_ERR_UNSUPPORTED;
+  if (qlora::linear_workspace_bytes(M, N, K, r) > qlora::kNoAllocScratchBytes)
+    return QLORA_ERR_WORKSPACE;
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  return hip_status(qlora::launch_fwd_noalloc(X, W, A, B, M, N, K, r, scale, Y, T_out,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X, const float* T,
                               const uint8_t* codes, const uint8_t* absmax_q,
                               const float* absmax_s2, const uint16_t* A, const uint16_t* B,

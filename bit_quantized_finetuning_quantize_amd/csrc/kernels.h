@@ -87,6 +87,13 @@ hipError_t launch_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
                       hipStream_t stream, hipEvent_t ev0 = nullptr,
                       hipEvent_t ev1 = nullptr, Dropout dr = Dropout{});
 
+// Forward with the library's own scratch array (one per device, this many
+// bytes) in place of a caller workspace.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t launch_fwd_noalloc(const uint16_t* X, Nf4Weight W, const uint16_t* A,
+                              const uint16_t* B, int64_t M, int64_t N, int64_t K, int r,
+                              float scale, uint16_t* Y, float* T_out, hipStream_t stream);
+
 // Records `ev` on `stream` when it is not null (profiling hooks around the
 // dominant launch of a call).
 inline hipError_t record_if(hipEvent_t ev, hipStream_t stream) {

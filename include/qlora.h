@@ -36,8 +36,9 @@
  * - Calls that share a workspace buffer must not overlap in time (same
  *   stream, or caller-side ordering). Otherwise calls are thread-safe: host
  *   threads may call concurrently on their own streams with their own
- *   buffers (the only process state is per-device flags, set once under an
- *   atomic, recording that a kernel's LDS limit has been raised).
+ *   buffers (the process state is per-device flags, set once under an
+ *   atomic, recording that a kernel's LDS limit has been raised, and the
+ *   scratch array of qlora_linear_fwd_noalloc with its cached address).
  *
  * The NF4 store
  * -------------
@@ -278,6 +279,27 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T,
                      const uint16_t* B, int64_t M, int64_t N, int64_t K,
                      int32_t r, float scale, uint16_t* dX, float* dA,
                      float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* qlora_linear_fwd_noalloc — qlora_linear_fwd without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). The
+ * scratch memory is a fixed device array of QLORA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends; the call
+ * itself allocates and frees nothing. Same kernels, same results bit for bit
+ * as qlora_linear_fwd. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (concurrent streams or host threads) race
+ * and give undefined results; calls ordered on one stream are safe. The
+ * array's contents on entry do not matter.
+ * Errors: as qlora_linear_fwd; WORKSPACE when the shape needs more than
+ * QLORA_NOALLOC_SCRATCH_BYTES (qlora_linear_workspace_bytes above it, e.g.
+ * beyond the 8192-token, 22016-wide linear at r = 64); QLORA_ERR_HIP also
+ * when the array's device address cannot be obtained on the current GPU. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int qlora_linear_fwd_noalloc(const uint16_t* X, const uint8_t* codes,
+                             const uint8_t* absmax_q, const float* absmax_s2,
+                             const uint16_t* A, const uint16_t* B, int64_t M,
+                             int64_t N, int64_t K, int32_t r, float scale,
+                             uint16_t* Y, float* T_out, void* stream);
 
 /* ---- profiling variants ------------------------------------------------------
  * Identical to qlora_linear_fwd / qlora_linear_bwd, and in addition record

@@ -112,6 +112,39 @@ def test_linear_fwd_rejects(lib):
     assert lib.qlora_linear_workspace_bytes(1, 1 << 21, 1 << 11, 8) == 0
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # QLORA_NOALLOC_SCRATCH_BYTES in include/qlora.h
+
+
+def _fwd_noalloc(lib, M=32, N=128, K=128, r=8, X=FAKE, codes=FAKE, A=FAKE):
+    return lib.qlora_linear_fwd_noalloc(X, codes, FAKE, FAKE, A, FAKE, M, N, K, r, 1.0, FAKE,
+                                        None, None)
+
+
+def test_header_states_noalloc_scratch_size():
+    text = open(HEADER).read()
+    m = re.search(r"#define QLORA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == NOALLOC_SCRATCH_BYTES
+
+
+def test_linear_fwd_noalloc_rejects(lib):
+    """The forward without a workspace validates like the forward and rejects
+    shapes whose workspace exceeds the fixed scratch array, before any GPU
+    call."""
+    assert _fwd_noalloc(lib, X=None) == -1
+    assert _fwd_noalloc(lib, codes=None) == -1
+    assert _fwd_noalloc(lib, M=0) == -1
+    assert _fwd_noalloc(lib, K=100) == -2
+    assert _fwd_noalloc(lib, r=257) == -2
+    assert _fwd_noalloc(lib, X=ODD) == -2
+    M, N, K, r = 16384, 22016, 8192, 256
+    assert lib.qlora_linear_workspace_bytes(M, N, K, r) > NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(lib, M, N, K, r) == -3
+    # every workload shape fits
+    for M, N, K, r in ((16, 4096, 4096, 16), (2048, 11008, 4096, 64), (2048, 4096, 11008, 64),
+                       (4096, 22016, 8192, 64), (4096, 8192, 22016, 64)):
+        assert 0 < lib.qlora_linear_workspace_bytes(M, N, K, r) <= NOALLOC_SCRATCH_BYTES
+
+
 def test_linear_bwd_rejects(lib):
     b = lib.qlora_linear_bwd
     args = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128, 128, 8, 1.0, FAKE, FAKE,
