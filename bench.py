@@ -353,7 +353,35 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
     res["adamw8"] = dict(params=na, ms=a8ms, bytes_per_param=round(b8, 4),
                          GBps=b8 * na / (a8ms * 1e-3) / 1e9,
                          state_bytes=2 * na + 8 * ((na + 255) // 256))
-    del m8, sm8, v8, sv8, st_p, st_g, st_16
+    del m8, sm8, v8, sv8
+    # the same two steps with the optimizer state in pinned host memory
+    # (hipHostMalloc, mapped): the moments cross the host link on every step
+    host = {}
+    for name in ("adamw_host", "adamw8_host"):
+        if name == "adamw_host":
+            hm, hv = q.adamw_state(na, dev, host=True)
+            fn = lambda t: q.qlora_adamw_step(st_p, hm, hv, st_g, 2e-4, step=t, weight_decay=0.01,
+                                              p_bf16=st_16)
+            state_bytes = 8 * na  # m and v, read and written
+        else:
+            hm8, hsm8, hv8, hsv8 = q.adamw8_state(na, dev, host=True)
+            fn = lambda t: q.qlora_adamw8_step(st_p, hm8, hsm8, hv8, hsv8, st_g, 2e-4, step=t,
+                                               weight_decay=0.01, p_bf16=st_16)
+            state_bytes = 2 * na + 8 * ((na + 255) // 256)
+        fn(1)
+        torch.cuda.synchronize()
+        qa.record()
+        for t in range(2, 5):
+            fn(t)
+        qb.record()
+        torch.cuda.synchronize()
+        hms = qa.elapsed_time(qb) / 3
+        host[name] = dict(params=na, ms=hms, state_bytes=state_bytes,
+                          host_link_GBps=2 * state_bytes / (hms * 1e-3) / 1e9,
+                          what="moments in pinned host memory, read and written in place")
+        log(f"[bench] {name}: {hms:.2f} ms per step")
+    res.update(host)
+    del st_p, st_g, st_16
     res["merge"] = dict(shape=[11008, 4096], rank=r, ms=mms,
                         GBps=(st0.nbytes() + 2 * W0.numel()) / (mms * 1e-3) / 1e9,
                         rank_flops_TFLOPs=2 * W0.numel() * r / (mms * 1e-3) / 1e12)
@@ -708,6 +736,8 @@ def main():
         "merge": pre["merge"],
         "adamw": pre["adamw"],
         "adamw8": pre["adamw8"],
+        "adamw_host": pre["adamw_host"],
+        "adamw8_host": pre["adamw8_host"],
         "dropout": pre["dropout"],
         "nodq": pre["nodq"],
         "gemv": gemv,

@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     Nf4Store,
     QloraError,
     adamw8_state,
+    adamw_state,
     empty_store,
     qlora_adamw8_step,
     qlora_adamw_step,

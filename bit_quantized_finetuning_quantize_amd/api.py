@@ -34,6 +34,33 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+_HIP = None
+
+
+def _state_ptr(t, name):
+    """Device-side address of an optimizer-state tensor: a contiguous GPU
+    tensor, or a contiguous pinned host tensor (hipHostMalloc, e.g. torch's
+    pin_memory=True), which the kernel then reads and writes over the host
+    link; its device address comes from hipHostGetDevicePointer."""
+    global _HIP
+    if not t.is_contiguous():
+        raise QloraError(f"{name} must be contiguous")
+    if t.is_cuda:
+        return ctypes.c_void_p(t.data_ptr())
+    if not t.is_pinned():
+        raise QloraError(f"{name} on the host must be pinned memory (pin_memory=True)")
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+        _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
+    dptr = ctypes.c_void_p()
+    rc = _HIP.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+    if rc != 0 or not dptr.value:
+        raise QloraError(f"{name}: hipHostGetDevicePointer failed ({rc})")
+    return dptr
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
         raise QloraError(f"{name} must be a contiguous {dtype} tensor on the GPU")
@@ -135,18 +162,29 @@ def qlora_adamw_step(p, m, v, g, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_de
             raise QloraError("p, m, v, g must be float32 tensors of one size")
     if p_bf16 is not None and p_bf16.numel() != n:
         raise QloraError("p_bf16 must have as many elements as p")
-    _check(LIB.qlora_adamw_step(_ptr(p), _ptr(m), _ptr(v), _ptr(g), n, float(lr), float(beta1),
+    _check(LIB.qlora_adamw_step(_ptr(p), _state_ptr(m, "m"), _state_ptr(v, "v"), _ptr(g), n,
+                                float(lr), float(beta1),
                                 float(beta2), float(eps), float(weight_decay), int(step),
                                 _ptr(p_bf16) if p_bf16 is not None else None, _stream()))
 
 
-def adamw8_state(n, device):
-    """Zero 8-bit AdamW state for n parameters: (m8, m_scale, v8, v_scale)."""
+def adamw_state(n, device, host=False):
+    """Zero float32 AdamW moments (m, v) for n parameters, on the GPU or
+    (host=True) in pinned host memory."""
+    if host:
+        return tuple(torch.zeros(n, dtype=torch.float32, pin_memory=True) for _ in range(2))
+    return tuple(torch.zeros(n, dtype=torch.float32, device=device) for _ in range(2))
+
+
+def adamw8_state(n, device, host=False):
+    """Zero 8-bit AdamW state for n parameters: (m8, m_scale, v8, v_scale),
+    on the GPU or (host=True) in pinned host memory."""
     nb = (n + 255) // 256
-    return (torch.zeros(n, dtype=torch.uint8, device=device),
-            torch.zeros(nb, dtype=torch.float32, device=device),
-            torch.zeros(n, dtype=torch.uint8, device=device),
-            torch.zeros(nb, dtype=torch.float32, device=device))
+    kw = dict(pin_memory=True) if host else dict(device=device)
+    return (torch.zeros(n, dtype=torch.uint8, **kw),
+            torch.zeros(nb, dtype=torch.float32, **kw),
+            torch.zeros(n, dtype=torch.uint8, **kw),
+            torch.zeros(nb, dtype=torch.float32, **kw))
 
 
 def qlora_adamw8_step(p, m8, m_scale, v8, v_scale, g, lr, beta1=0.9, beta2=0.999, eps=1e-8,
@@ -155,17 +193,18 @@ def qlora_adamw8_step(p, m8, m_scale, v8, v_scale, g, lr, beta1=0.9, beta2=0.999
     n = p.numel()
     _need(p, torch.float32, "p")
     _need(g, torch.float32, "g")
-    _need(m_scale, torch.float32, "m_scale")
-    _need(v_scale, torch.float32, "v_scale")
-    _need(m8, torch.uint8, "m8")
-    _need(v8, torch.uint8, "v8")
+    for t, dt, name in ((m_scale, torch.float32, "m_scale"), (v_scale, torch.float32, "v_scale"),
+                        (m8, torch.uint8, "m8"), (v8, torch.uint8, "v8")):
+        if t.dtype != dt:
+            raise QloraError(f"{name} must be a {dt} tensor")
     if g.numel() != n or m8.numel() != n or v8.numel() != n:
         raise QloraError("p, g, m8 and v8 must have the same number of elements")
     if m_scale.numel() != (n + 255) // 256 or v_scale.numel() != (n + 255) // 256:
         raise QloraError("one scale per block of 256 parameters")
     if p_bf16 is not None:
         _need(p_bf16, torch.bfloat16, "p_bf16")
-    _check(LIB.qlora_adamw8_step(_ptr(p), _ptr(m8), _ptr(m_scale), _ptr(v8), _ptr(v_scale),
+    _check(LIB.qlora_adamw8_step(_ptr(p), _state_ptr(m8, "m8"), _state_ptr(m_scale, "m_scale"),
+                                 _state_ptr(v8, "v8"), _state_ptr(v_scale, "v_scale"),
                                  _ptr(g), n, float(lr), float(beta1), float(beta2), float(eps),
                                  float(weight_decay), int(step),
                                  _ptr(p_bf16) if p_bf16 is not None else None, _stream()))

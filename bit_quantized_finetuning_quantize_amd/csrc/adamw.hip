@@ -17,9 +17,9 @@
 //   p2 = p1 - fl(lr * fl(fl(m1 / c1) / den))  c1 = fl(1 - b1^t)
 // and optionally the bf16 copy of p2 (round to nearest even) that the
 // linear calls take as A or B. The host constants are computed in float64
-// and rounded once. The state may live in any memory the device can access
-// (device, or managed memory that pages to the host): the kernel only
-// streams through it.
+// and rounded once. The state may be device memory or pinned host memory
+// mapped into the device's address space: the kernel streams through it in
+// place either way.
 #include <cmath>
 
 #include "common.h"

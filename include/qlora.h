@@ -180,8 +180,15 @@ int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* 
  *   v  = beta2*v + (1-beta2)*(g*g)
  *   p  = p1 - lr*((m/c1) / (sqrt(v/c2) + eps))
  * p_bf16 (optional, device uint16 [n]) receives bf16(p), the copy that the
- * linear calls take as A or B. The state may be device memory or managed
- * memory that pages to the host; the call only streams through it.
+ * linear calls take as A or B.
+ * Host-resident state (the paged optimizer of ozercemkelahmet.com "QLoRA",
+ * How it works, Step 7, keeps optimizer state in host memory when the
+ * device runs short): m and v may be pinned host memory from hipHostMalloc,
+ * mapped into the device's address space, passed as the address that
+ * hipHostGetDevicePointer returns. The kernel then reads and writes the
+ * moments in place over the host link (no copy, no managed memory, no
+ * demand paging); results are the same bit for bit. p, g and p_bf16 stay
+ * device memory.
  * Errors: INVALID_ARG for a null pointer, n <= 0, step < 1, beta outside
  * [0, 1) or eps <= 0; UNSUPPORTED for float arrays not 4-byte aligned or
  * p_bf16 not 2-byte aligned. */
@@ -209,6 +216,8 @@ int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, fl
  * enc rounds to the nearest code, ties to the even code, saturating at the
  * largest finite one. 18 bytes of traffic per parameter against 30 for the
  * float32 state (with the bf16 copy).
+ * m8, m_scale, v8 and v_scale may be pinned host memory as m and v of
+ * qlora_adamw_step.
  * Errors: as qlora_adamw_step (m8 and v8 need no alignment; the scales are
  * float arrays). */
 int qlora_adamw8_step(float* p, uint8_t* m8, float* m_scale, uint8_t* v8, float* v_scale,
