@@ -599,6 +599,147 @@ def run_gemv(args, q, synthetic, torch, dev):
     return out
 
 
+def run_stack7b(args, q, synthetic, torch, dev):
+    """The 7B-style decoder stack: 32 layers x (q, k, v, o 4096x4096; gate, up
+    11008x4096; down 4096x11008), N(0, 0.02) weights quantized to NF4 and kept
+    resident (3,340,771,328 bytes), LoRA r=64 alpha=16 on every linear, 2048
+    tokens. One sweep: the forward of every linear from layer 0 to layer 31,
+    then the backward (dX, dA, dB) from layer 31 back to layer 0, so each
+    store streams from HBM twice per sweep. Each linear type draws its own
+    activations (the same for every layer: an activation feeding a layer has
+    just been written, so it is cache-resident either way); the weights,
+    adapters and outputs are per layer."""
+    M, r, alpha = 2048, 64, 16
+    s = alpha / r
+    shapes = synthetic.LLAMA7B
+    acts = []
+    for j, (N, K) in enumerate(shapes):
+        base = synthetic.linear_base(0, j)
+        acts.append(dict(X=synthetic.normal((M, K), 1.0, dev, 0, base + synthetic.X_IDX),
+                         dY=synthetic.normal((M, N), 1e-3, dev, 0, base + synthetic.DY_IDX)))
+    lin = []
+    for layer in range(32):
+        for j, (N, K) in enumerate(shapes):
+            base = synthetic.linear_base(layer, j)
+            W = synthetic.normal((N, K), 0.02, dev, 0, base + synthetic.W_IDX)
+            st = q.qlora_nf4_quantize(W)
+            del W
+            lin.append(dict(N=N, K=K, j=j, st=st,
+                            A=synthetic.normal((K, r), 0.01, dev, 0, base + synthetic.A_IDX),
+                            B=synthetic.normal((r, N), 0.01, dev, 0, base + synthetic.B_IDX),
+                            T=torch.empty(M, r, dtype=torch.float32, device=dev),
+                            dA=torch.empty(K, r, dtype=torch.float32, device=dev),
+                            dB=torch.empty(r, N, dtype=torch.float32, device=dev)))
+    store_bytes = sum(L["st"].nbytes() for L in lin)
+    Ybuf = {n: torch.empty(M, n, dtype=torch.bfloat16, device=dev) for n in (4096, 11008)}
+    dXbuf = {k: torch.empty(M, k, dtype=torch.bfloat16, device=dev) for k in (4096, 11008)}
+    ws = q.workspace(M, 11008, 11008, r, dev)
+    flops = sum(4 * M * L["N"] * L["K"] + 6 * M * r * (L["K"] + L["N"]) for L in lin)
+
+    def sweep():
+        for L in lin:
+            a = acts[L["j"]]
+            q.qlora_linear_fwd(a["X"], L["st"], L["A"], L["B"], s, Y=Ybuf[L["N"]], T=L["T"], ws=ws)
+        for L in reversed(lin):
+            a = acts[L["j"]]
+            q.qlora_linear_bwd(a["dY"], a["X"], L["T"], L["st"], L["A"], L["B"], s,
+                               dX=dXbuf[L["K"]], dA=L["dA"], dB=L["dB"], ws=ws)
+
+    sweep()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.stack_sweeps):
+        sweep()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.stack_sweeps
+    out = dict(workload="32 layers x 7 linears (4096x4096 x4, 11008x4096 x2, 4096x11008), "
+                        "2048 tokens, r=64: forward L0..L31 then backward L31..L0",
+               ms_per_sweep=round(ms, 3), flops_per_sweep=flops,
+               tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+               frac_of_bf16_peak=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               store_bytes=store_bytes, sweeps=args.stack_sweeps)
+    log(f"[bench] 7B-style sweep: {ms:.2f} ms, {out['tflops']} TFLOP/s")
+    del lin, acts, Ybuf, dXbuf, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_stress65b(args, q, synthetic, torch, dev):
+    """The 65B-shaped stack: all 560 Student-t(5) x 0.02 weights of 80 layers
+    x (q, k, v, o 8192x8192; gate, up 22016x8192; down 8192x22016) quantized
+    on the device and kept resident (33,407,713,280 bytes); the quantization
+    kernels are timed alone (each layer's weights drawn first, then its
+    seven quantizations between two events). Then layer 0 forward and
+    backward at 4096 tokens (4 x 1024), r=64 alpha=16."""
+    shapes = synthetic.LLAMA65B
+    stores = []
+    qms, nel = 0.0, 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for layer in range(80):
+        Ws = [synthetic.student_t((N, K), 5, 0.02, dev, 0,
+                                  synthetic.linear_base(layer, j) + synthetic.W_IDX)
+              for j, (N, K) in enumerate(shapes)]
+        torch.cuda.synchronize()
+        e0.record()
+        for W in Ws:
+            stores.append(q.qlora_nf4_quantize(W))
+        e1.record()
+        torch.cuda.synchronize()
+        qms += e0.elapsed_time(e1)
+        nel += sum(W.numel() for W in Ws)
+        del Ws
+    store_bytes = sum(st.nbytes() for st in stores)
+    quant = dict(weights=len(stores), params=nel, store_bytes=store_bytes, ms=round(qms, 3),
+                 GBps=round((2 * nel + store_bytes) / (qms * 1e-3) / 1e9, 1),
+                 what="bf16 read + NF4 store written, kernels between events per layer")
+    log(f"[bench] 65B-shaped quantize all: {qms:.1f} ms, {quant['GBps']} GB/s, "
+        f"{store_bytes} B resident")
+    M, r, alpha = 4096, 64, 16
+    s = alpha / r
+    lay = []
+    for j, (N, K) in enumerate(shapes):
+        base = synthetic.linear_base(0, j)
+        lay.append(dict(N=N, K=K, st=stores[j],
+                        X=synthetic.normal((M, K), 1.0, dev, 0, base + synthetic.X_IDX),
+                        dY=synthetic.normal((M, N), 1e-3, dev, 0, base + synthetic.DY_IDX),
+                        A=synthetic.normal((K, r), 0.01, dev, 0, base + synthetic.A_IDX),
+                        B=synthetic.normal((r, N), 0.01, dev, 0, base + synthetic.B_IDX),
+                        Y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+                        T=torch.empty(M, r, dtype=torch.float32, device=dev),
+                        dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                        dA=torch.empty(K, r, dtype=torch.float32, device=dev),
+                        dB=torch.empty(r, N, dtype=torch.float32, device=dev)))
+    ws = q.workspace(M, 22016, 22016, r, dev)
+    flops = sum(4 * M * L["N"] * L["K"] + 6 * M * r * (L["K"] + L["N"]) for L in lay)
+
+    def layer_step():
+        for L in lay:
+            q.qlora_linear_fwd(L["X"], L["st"], L["A"], L["B"], s, Y=L["Y"], T=L["T"], ws=ws)
+        for L in reversed(lay):
+            q.qlora_linear_bwd(L["dY"], L["X"], L["T"], L["st"], L["A"], L["B"], s, dX=L["dX"],
+                               dA=L["dA"], dB=L["dB"], ws=ws)
+
+    layer_step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.stack_sweeps):
+        layer_step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.stack_sweeps
+    one = dict(workload="layer 0 of the 65B-shaped stack (8192x8192 x4, 22016x8192 x2, "
+                        "8192x22016), 4096 tokens, r=64, fwd + bwd, the other 79 layers' "
+                        "stores resident",
+               ms=round(ms, 3), flops=flops, tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+               frac_of_bf16_peak=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    log(f"[bench] 65B-shaped layer fwd+bwd at 4096 tokens: {ms:.2f} ms, {one['tflops']} TFLOP/s")
+    del lay, stores, ws
+    torch.cuda.empty_cache()
+    return dict(quantize_all=quant, layer=one)
+
+
 def cpu_baseline(args, projs, torch):
     """The oracle, timed on this host on a bounded sample: forward and
     backward of the three projections, r=64, for the first `cpu_rows` tokens
@@ -648,6 +789,11 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--no-stacks", action="store_true",
+                    help="skip the 7B-style sweep and the 65B-shaped legs")
+    ap.add_argument("--only-stacks", action="store_true",
+                    help="run only the 7B-style sweep and the 65B-shaped legs")
+    ap.add_argument("--stack-sweeps", type=int, default=3)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the dispatches the counter runs read")
     ap.add_argument("--pmc-summarize", nargs=4,
@@ -671,6 +817,10 @@ def main():
     import synthetic
 
     dev = torch.device("cuda:0")
+    if args.only_stacks:
+        print(json.dumps({"stack_7b": run_stack7b(args, q, synthetic, torch, dev),
+                          "stress_65b": run_stress65b(args, q, synthetic, torch, dev)}), flush=True)
+        return
     ev = HipEvents()
     log("[bench] prefill MLP fwd+bwd ...")
     pre, projs = run_prefill(args, q, synthetic, torch, dev, ev)
@@ -680,6 +830,11 @@ def main():
     if not args.no_gemv:
         log("[bench] decode GEMV ...")
         gemv = run_gemv(args, q, synthetic, torch, dev)
+    stacks = None
+    if not args.no_stacks:
+        log("[bench] 7B-style stack sweep and 65B-shaped legs ...")
+        stacks = {"stack_7b": run_stack7b(args, q, synthetic, torch, dev),
+                  "stress_65b": run_stress65b(args, q, synthetic, torch, dev)}
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU oracle sample ...")
@@ -741,6 +896,7 @@ def main():
         "dropout": pre["dropout"],
         "nodq": pre["nodq"],
         "gemv": gemv,
+        "stacks": stacks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
