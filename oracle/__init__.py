@@ -49,4 +49,6 @@ from .dropout import (  # noqa: F401
     unpack_keep,
 )
 from . import fp8  # noqa: F401
+from . import fp4  # noqa: F401
+from . import store  # noqa: F401
 from .adamw8 import BLOCK8, adamw8_step, dequantize_state, num_blocks8, quantize_state  # noqa: F401
