@@ -4,6 +4,9 @@
 from .api import (  # noqa: F401
     BLOCK,
     GROUP,
+    STORE_DQ_FP8,
+    STORE_FP4,
+    STORE_NF4,
     Nf4Store,
     QloraError,
     adamw8_state,

@@ -27,6 +27,16 @@ SIGNATURES = {
     "qlora_nf4_quantize": (_c_int, [_vp, _c_i64, _vp, _vp, _vp, _vp]),
     "qlora_nf4_dequantize": (_c_int, [_vp, _vp, _vp, _c_i64, _vp, _vp]),
     "qlora_nf4_dequantize_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp, _vp]),
+    "qlora_nf4_quantize_ex": (_c_int, [_vp, _c_i64, _vp, _vp, _vp, _c_i32, _vp]),
+    "qlora_nf4_dequantize_ex": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i32, _vp, _vp]),
+    "qlora_nf4_dequantize_bf16_ex": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i32, _vp, _vp]),
+    "qlora_nf4_merge_ex": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i32, _c_f32,
+                                    _c_i32, _vp, _vp]),
+    "qlora_linear_fwd_ex": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                     _c_i32, _c_f32, _vp, _vp, _vp, _c_size, _c_i32, _vp]),
+    "qlora_linear_bwd_ex": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
+                                     _c_i64, _c_i32, _c_f32, _vp, _vp, _vp, _vp, _c_size,
+                                     _c_i32, _vp]),
     "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_f32, _c_f32, _c_f32, _c_f32,
                                   _c_f32, _c_i64, _vp, _vp]),
     "qlora_adamw8_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_f32, _c_f32, _c_f32,

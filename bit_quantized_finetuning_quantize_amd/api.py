@@ -13,6 +13,10 @@ from ._lib import LIB
 
 BLOCK = 64
 GROUP = 256
+# store types (include/qlora.h): bit flags
+STORE_NF4 = 0
+STORE_FP4 = 1
+STORE_DQ_FP8 = 2
 
 
 class QloraError(RuntimeError):
@@ -85,14 +89,16 @@ def qlora_nf4_codebook():
 
 
 class Nf4Store:
-    """The device buffers of one NF4 tensor (owned by torch). Without double
-    quantization `absmax_q` is None and `absmax_s2` holds one float32
-    constant per 64-block."""
+    """The device buffers of one 4-bit tensor (owned by torch). Without
+    double quantization `absmax_q` is None and `absmax_s2` holds one float32
+    constant per 64-block. `store_type`: STORE_NF4 (0), or the flags
+    STORE_FP4 (FP4 levels) and STORE_DQ_FP8 (E4M3 constant code)."""
 
-    def __init__(self, codes, absmax_q, absmax_s2, numel, shape=None):
+    def __init__(self, codes, absmax_q, absmax_s2, numel, shape=None, store_type=STORE_NF4):
         self.codes, self.absmax_q, self.absmax_s2 = codes, absmax_q, absmax_s2
         self.numel = int(numel)
         self.shape = tuple(shape) if shape is not None else (self.numel,)
+        self.store_type = int(store_type)
 
     @property
     def double_quant(self):
@@ -103,7 +109,7 @@ class Nf4Store:
         return self.codes.numel() + q8 + 4 * self.absmax_s2.numel()
 
 
-def empty_store(numel, device, shape=None, double_quant=True):
+def empty_store(numel, device, shape=None, double_quant=True, store_type=STORE_NF4):
     codes = torch.empty(qlora_nf4_codes_bytes(numel), dtype=torch.uint8, device=device)
     if double_quant:
         q8 = torch.empty(qlora_nf4_num_blocks(numel), dtype=torch.uint8, device=device)
@@ -111,32 +117,38 @@ def empty_store(numel, device, shape=None, double_quant=True):
     else:
         q8 = None
         s2 = torch.empty(qlora_nf4_num_blocks(numel), dtype=torch.float32, device=device)
-    return Nf4Store(codes, q8, s2, numel, shape)
+    return Nf4Store(codes, q8, s2, numel, shape, store_type)
 
 
-def qlora_nf4_quantize(w, out=None, double_quant=True):
+def qlora_nf4_quantize(w, out=None, double_quant=True, store_type=STORE_NF4):
     """Quantize a bf16 tensor (any shape, flattened row-major); with
-    double_quant=False the store keeps the float32 block constants."""
+    double_quant=False the store keeps the float32 block constants;
+    store_type selects FP4 levels and / or the E4M3 constant code."""
     _need(w, torch.bfloat16, "w")
-    st = out if out is not None else empty_store(w.numel(), w.device, w.shape, double_quant)
-    _check(LIB.qlora_nf4_quantize(_ptr(w), w.numel(), _ptr(st.codes), _ptr(st.absmax_q),
-                                  _ptr(st.absmax_s2), _stream()))
+    if out is None:
+        st = empty_store(w.numel(), w.device, w.shape, double_quant, store_type)
+    else:
+        st = out
+        st.store_type = int(store_type)
+    _check(LIB.qlora_nf4_quantize_ex(_ptr(w), w.numel(), _ptr(st.codes), _ptr(st.absmax_q),
+                                     _ptr(st.absmax_s2), st.store_type, _stream()))
     return st
 
 
 def qlora_nf4_dequantize(st, out=None):
     out = out if out is not None else torch.empty(st.numel, dtype=torch.float32,
                                                   device=st.codes.device)
-    _check(LIB.qlora_nf4_dequantize(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2),
-                                    st.numel, _ptr(out), _stream()))
+    _check(LIB.qlora_nf4_dequantize_ex(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2),
+                                       st.numel, st.store_type, _ptr(out), _stream()))
     return out
 
 
 def qlora_nf4_dequantize_bf16(st, out=None):
     out = out if out is not None else torch.empty(st.numel, dtype=torch.bfloat16,
                                                   device=st.codes.device)
-    _check(LIB.qlora_nf4_dequantize_bf16(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2),
-                                         st.numel, _ptr(out), _stream()))
+    _check(LIB.qlora_nf4_dequantize_bf16_ex(_ptr(st.codes), _ptr(st.absmax_q),
+                                            _ptr(st.absmax_s2), st.numel, st.store_type,
+                                            _ptr(out), _stream()))
     return out
 
 
@@ -147,8 +159,9 @@ def qlora_nf4_merge(st, A, B, scale, out=None):
     r = A.shape[1]
     out = out if out is not None else torch.empty(N, K, dtype=torch.bfloat16,
                                                   device=st.codes.device)
-    _check(LIB.qlora_nf4_merge(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2), N, K,
-                               _ptr(A), _ptr(B), r, float(scale), _ptr(out), _stream()))
+    _check(LIB.qlora_nf4_merge_ex(_ptr(st.codes), _ptr(st.absmax_q), _ptr(st.absmax_s2), N, K,
+                                  _ptr(A), _ptr(B), r, float(scale), st.store_type, _ptr(out),
+                                  _stream()))
     return out
 
 
@@ -235,6 +248,14 @@ def qlora_linear_fwd(X, W, A, B, scale, want_T=True, Y=None, T=None, ws=None, ev
     if want_T and T is None:
         T = torch.empty(M, r, dtype=torch.float32, device=X.device)
     ws = ws if ws is not None else workspace(M, N, K, r, X.device)
+    if W.store_type != STORE_NF4:
+        if events is not None:
+            raise QloraError("profiling events are taken on NF4 stores only")
+        _check(LIB.qlora_linear_fwd_ex(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q),
+                                       _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r,
+                                       float(scale), _ptr(Y), _ptr(T) if want_T else None,
+                                       _ptr(ws), ws.numel(), W.store_type, _stream()))
+        return Y, (T if want_T else None)
     ev = events if events is not None else (None, None)
     _check(LIB.qlora_linear_fwd_profiled(_ptr(X), _ptr(W.codes), _ptr(W.absmax_q),
                                          _ptr(W.absmax_s2), _ptr(A), _ptr(B), M, N, K, r,
@@ -277,6 +298,15 @@ def qlora_linear_bwd(dY, X, T, W, A, B, scale, want_dX=True, dX=None, dA=None, d
     dA = dA if dA is not None else torch.empty(K, r, dtype=torch.float32, device=X.device)
     dB = dB if dB is not None else torch.empty(r, N, dtype=torch.float32, device=X.device)
     ws = ws if ws is not None else workspace(M, N, K, r, X.device)
+    if W.store_type != STORE_NF4:
+        if events is not None:
+            raise QloraError("profiling events are taken on NF4 stores only")
+        _check(LIB.qlora_linear_bwd_ex(_ptr(dY), _ptr(X), _ptr(T), _ptr(W.codes),
+                                       _ptr(W.absmax_q), _ptr(W.absmax_s2), _ptr(A), _ptr(B),
+                                       M, N, K, r, float(scale), _ptr(dX) if want_dX else None,
+                                       _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), W.store_type,
+                                       _stream()))
+        return (dX if want_dX else None), dA, dB
     ev = events if events is not None else (None, None)
     _check(LIB.qlora_linear_bwd_profiled(_ptr(dY), _ptr(X), _ptr(T), _ptr(W.codes),
                                          _ptr(W.absmax_q), _ptr(W.absmax_s2), _ptr(A), _ptr(B),

@@ -109,47 +109,7 @@ adamw_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v
 // wave-wide reduction. The parameter, gradient and code accesses are
 // non-temporal: each byte is read and written once per step.
 
-// dec: the value of a code, exactly (the exponent field goes straight into
-// the float's exponent; subnormals are m 2^(1 - bias - mbits)).
-template <int kE, int kM, int kBias>
-__device__ __forceinline__ float ofp8_decode(uint32_t c) {
-  const uint32_t s = (c >> 7) & 1u;
-  const uint32_t e = (c >> kM) & ((1u << kE) - 1u);
-  const uint32_t m = c & ((1u << kM) - 1u);
-  const float sub = (float)m * __builtin_bit_cast(float, (uint32_t)(127 + 1 - kBias - kM) << 23);
-  const float nrm = __builtin_bit_cast(float, ((e + 127u - kBias) << 23) | (m << (23 - kM)));
-  const float mag = e ? nrm : sub;
-  return s ? -mag : mag;
-}
-
-// enc for a finite float: the mantissa rounded to kM bits on its integer
-// bits (ties to even), a carry running into the exponent field; values
-// below the smallest normal rounded on the subnormal grid.
-template <int kE, int kM, int kBias, uint32_t kTopCode>
-__device__ __forceinline__ uint32_t ofp8_encode(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (u >> 31) << 7;
-  const uint32_t ua = u & 0x7fffffffu;
-  const float a = __builtin_bit_cast(float, ua);
-  const float top = ofp8_decode<kE, kM, kBias>(kTopCode);
-  const float min_normal = __builtin_bit_cast(float, (uint32_t)(127 + 1 - kBias) << 23);
-  uint32_t mag;
-  if (!(a < top)) {
-    mag = kTopCode;
-  } else if (a < min_normal) {
-    // a 2^(bias - 1 + kM) is exact; rintf rounds half to even
-    mag = (uint32_t)__builtin_rintf(a * __builtin_bit_cast(float, (uint32_t)(127 - 1 + kBias + kM) << 23));
-  } else {
-    const uint32_t e = (ua >> 23) - 127u + kBias;     // biased exponent of the code
-    const uint32_t q = (ua >> (23 - kM)) & ((1u << kM) - 1u);
-    const uint32_t rem = ua & ((1u << (23 - kM)) - 1u);
-    const uint32_t half = 1u << (22 - kM);
-    const uint32_t up = (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
-    mag = ((e << kM) + q + up);
-    mag = mag > kTopCode ? kTopCode : mag;
-  }
-  return mag | sign;
-}
+// ofp8_decode / ofp8_encode (common.h) hold the OFP8 conversions.
 
 constexpr int kBlock8 = 256;
 

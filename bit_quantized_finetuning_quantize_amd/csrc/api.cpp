@@ -33,6 +33,8 @@ int check_store(const uint8_t* codes, const uint8_t* absmax_q, const float* absm
   return QLORA_OK;
 }
 
+bool valid_store_type(int32_t t) { return t >= 0 && t <= (QLORA_STORE_FP4 | QLORA_STORE_DQ_FP8); }
+
 int check_linear_shape(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M <= 0 || N <= 0 || K <= 0) return QLORA_ERR_INVALID_ARG;
   if (K % QLORA_NF4_BLOCK != 0 || N % QLORA_NF4_BLOCK != 0) return QLORA_ERR_UNSUPPORTED;
@@ -84,39 +86,68 @@ void qlora_nf4_codebook(float* levels) {
   std::memcpy(levels, qlora::kNF4, sizeof(qlora::kNF4));
 }
 
-int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
-                       float* absmax_s2, void* stream) {
+int qlora_nf4_quantize_ex(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
+                          float* absmax_s2, int32_t store_type, void* stream) {
   if (!w || numel <= 0) return QLORA_ERR_INVALID_ARG;
   if (!codes || !absmax_s2) return QLORA_ERR_INVALID_ARG;  // absmax_q null: no DQ
+  if (!valid_store_type(store_type)) return QLORA_ERR_INVALID_ARG;
   if (!aligned(w, 2) || !aligned(codes, 4) || !aligned(absmax_s2, 4)) return QLORA_ERR_UNSUPPORTED;
   if (qlora_nf4_num_groups(numel) > kMaxGroups) return QLORA_ERR_UNSUPPORTED;
-  return hip_status(qlora::launch_nf4_quantize(w, numel, codes, absmax_q, absmax_s2,
+  return hip_status(qlora::launch_nf4_quantize(w, numel, codes, absmax_q, absmax_s2, store_type,
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
+                       float* absmax_s2, void* stream) {
+  return qlora_nf4_quantize_ex(w, numel, codes, absmax_q, absmax_s2, QLORA_STORE_NF4, stream);
+}
+
 static int dequant_common(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
-                          int64_t numel, void* out, bool bf16, void* stream) {
+                          int64_t numel, int32_t store_type, void* out, bool bf16, void* stream) {
   if (!codes || !absmax_s2 || !out || numel <= 0) return QLORA_ERR_INVALID_ARG;
+  if (!valid_store_type(store_type)) return QLORA_ERR_INVALID_ARG;
   if (!aligned(codes, 4) || !aligned(absmax_s2, 4) || !aligned(out, 16)) return QLORA_ERR_UNSUPPORTED;
-  return hip_status(qlora::launch_nf4_dequantize(codes, absmax_q, absmax_s2, numel, out, bf16,
+  return hip_status(qlora::launch_nf4_dequantize(qlora::Nf4Weight{codes, absmax_q, absmax_s2,
+                                                                  store_type},
+                                                 numel, out, bf16,
                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qlora_nf4_dequantize_ex(const uint8_t* codes, const uint8_t* absmax_q,
+                            const float* absmax_s2, int64_t numel, int32_t store_type,
+                            float* out, void* stream) {
+  return dequant_common(codes, absmax_q, absmax_s2, numel, store_type, out, false, stream);
+}
+
+int qlora_nf4_dequantize_bf16_ex(const uint8_t* codes, const uint8_t* absmax_q,
+                                 const float* absmax_s2, int64_t numel, int32_t store_type,
+                                 uint16_t* out, void* stream) {
+  return dequant_common(codes, absmax_q, absmax_s2, numel, store_type, out, true, stream);
 }
 
 int qlora_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
                          int64_t numel, float* out, void* stream) {
-  return dequant_common(codes, absmax_q, absmax_s2, numel, out, false, stream);
+  return dequant_common(codes, absmax_q, absmax_s2, numel, QLORA_STORE_NF4, out, false, stream);
 }
 
 int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
                               const float* absmax_s2, int64_t numel, uint16_t* out,
                               void* stream) {
-  return dequant_common(codes, absmax_q, absmax_s2, numel, out, true, stream);
+  return dequant_common(codes, absmax_q, absmax_s2, numel, QLORA_STORE_NF4, out, true, stream);
 }
 
 int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
                     int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
                     float scale, uint16_t* out, void* stream) {
+  return qlora_nf4_merge_ex(codes, absmax_q, absmax_s2, N, K, A, B, r, scale, QLORA_STORE_NF4,
+                            out, stream);
+}
+
+int qlora_nf4_merge_ex(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                       int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
+                       float scale, int32_t store_type, uint16_t* out, void* stream) {
   if (!A || !B || !out) return QLORA_ERR_INVALID_ARG;
+  if (!valid_store_type(store_type)) return QLORA_ERR_INVALID_ARG;
   int st = check_store(codes, absmax_q, absmax_s2);
   if (st != QLORA_OK) return st;
   if (N <= 0 || K <= 0) return QLORA_ERR_INVALID_ARG;
@@ -124,8 +155,9 @@ int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* 
   if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30 || (N + 63) / 64 > 65535)
     return QLORA_ERR_UNSUPPORTED;
   if (!aligned(A, 2) || !aligned(B, 2) || !aligned(out, 16)) return QLORA_ERR_UNSUPPORTED;
-  return hip_status(qlora::launch_nf4_merge(codes, absmax_q, absmax_s2, N, K, A, B, r, scale,
-                                            out, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(qlora::launch_nf4_merge(qlora::Nf4Weight{codes, absmax_q, absmax_s2, store_type},
+                                            N, K, A, B, r, scale, out,
+                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
 int qlora_adamw_step(float* p, float* m, float* v, const float* g, int64_t n, float lr,
@@ -161,12 +193,13 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) 
   return qlora::linear_workspace_bytes(M, N, K, r);
 }
 
-int qlora_linear_fwd_profiled(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
-                              const float* absmax_s2, const uint16_t* A, const uint16_t* B,
-                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
-                              uint16_t* Y, float* T_out, void* ws, size_t ws_bytes, void* stream,
-                              void* ev_begin, void* ev_end) {
+static int linear_fwd_impl(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                           const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                           int64_t M, int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y,
+                           float* T_out, void* ws, size_t ws_bytes, int32_t store_type,
+                           void* stream, void* ev_begin, void* ev_end) {
   if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  if (!valid_store_type(store_type)) return QLORA_ERR_INVALID_ARG;
   int st = check_store(codes, absmax_q, absmax_s2);
   if (st != QLORA_OK) return st;
   st = check_linear_shape(M, N, K, r);
@@ -177,7 +210,7 @@ int qlora_linear_fwd_profiled(const uint16_t* X, const uint8_t* codes, const uin
   const size_t need = qlora::linear_workspace_bytes(M, N, K, r);
   if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
-  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2, store_type};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev_begin);
   hipEvent_t e1 = reinterpret_cast<hipEvent_t>(ev_end);
@@ -187,12 +220,29 @@ int qlora_linear_fwd_profiled(const uint16_t* X, const uint8_t* codes, const uin
   return hip_status(qlora::launch_fwd_gemm(X, W, A, B, M, N, K, r, scale, Y, T_out, ws, s, e0, e1));
 }
 
+int qlora_linear_fwd_profiled(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                              const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                              uint16_t* Y, float* T_out, void* ws, size_t ws_bytes, void* stream,
+                              void* ev_begin, void* ev_end) {
+  return linear_fwd_impl(X, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, Y, T_out, ws,
+                         ws_bytes, QLORA_STORE_NF4, stream, ev_begin, ev_end);
+}
+
 int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
                      const float* absmax_s2, const uint16_t* A, const uint16_t* B, int64_t M,
                      int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y, float* T_out,
                      void* ws, size_t ws_bytes, void* stream) {
-  return qlora_linear_fwd_profiled(X, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, Y,
-                                   T_out, ws, ws_bytes, stream, nullptr, nullptr);
+  return linear_fwd_impl(X, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, Y, T_out, ws,
+                         ws_bytes, QLORA_STORE_NF4, stream, nullptr, nullptr);
+}
+
+int qlora_linear_fwd_ex(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
+                        const float* absmax_s2, const uint16_t* A, const uint16_t* B, int64_t M,
+                        int64_t N, int64_t K, int32_t r, float scale, uint16_t* Y, float* T_out,
+                        void* ws, size_t ws_bytes, int32_t store_type, void* stream) {
+  return linear_fwd_impl(X, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, Y, T_out, ws,
+                         ws_bytes, store_type, stream, nullptr, nullptr);
 }
 
 int qlora_linear_fwd_noalloc(const uint16_t* X, const uint8_t* codes, const uint8_t* absmax_q,
@@ -215,13 +265,14 @@ int qlora_linear_fwd_noalloc(const uint16_t* X, const uint8_t* codes, const uint
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
-int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X, const float* T,
-                              const uint8_t* codes, const uint8_t* absmax_q,
-                              const float* absmax_s2, const uint16_t* A, const uint16_t* B,
-                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
-                              uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
-                              void* stream, void* ev_begin, void* ev_end) {
+static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* T,
+                           const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                           const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                           int32_t r, float scale, uint16_t* dX, float* dA, float* dB, void* ws,
+                           size_t ws_bytes, int32_t store_type, void* stream, void* ev_begin,
+                           void* ev_end) {
   if (!dY || !X || !A || !B || !dA || !dB) return QLORA_ERR_INVALID_ARG;
+  if (!valid_store_type(store_type)) return QLORA_ERR_INVALID_ARG;
   int st = check_store(codes, absmax_q, absmax_s2);
   if (st != QLORA_OK) return st;
   st = check_linear_shape(M, N, K, r);
@@ -232,11 +283,21 @@ int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X, const float
   const size_t need = qlora::linear_workspace_bytes(M, N, K, r);
   if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return QLORA_ERR_UNSUPPORTED;
-  qlora::Nf4Weight W{codes, absmax_q, absmax_s2};
+  qlora::Nf4Weight W{codes, absmax_q, absmax_s2, store_type};
   return hip_status(qlora::launch_bwd(dY, X, T, W, A, B, M, N, K, r, scale, dX, dA, dB, ws,
                                       reinterpret_cast<hipStream_t>(stream),
                                       reinterpret_cast<hipEvent_t>(ev_begin),
                                       reinterpret_cast<hipEvent_t>(ev_end)));
+}
+
+int qlora_linear_bwd_profiled(const uint16_t* dY, const uint16_t* X, const float* T,
+                              const uint8_t* codes, const uint8_t* absmax_q,
+                              const float* absmax_s2, const uint16_t* A, const uint16_t* B,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                              uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                              void* stream, void* ev_begin, void* ev_end) {
+  return linear_bwd_impl(dY, X, T, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, dX, dA,
+                         dB, ws, ws_bytes, QLORA_STORE_NF4, stream, ev_begin, ev_end);
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, const uint8_t* codes,
@@ -244,8 +305,17 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* T, cons
                      const uint16_t* B, int64_t M, int64_t N, int64_t K, int32_t r, float scale,
                      uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
                      void* stream) {
-  return qlora_linear_bwd_profiled(dY, X, T, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale,
-                                   dX, dA, dB, ws, ws_bytes, stream, nullptr, nullptr);
+  return linear_bwd_impl(dY, X, T, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, dX, dA,
+                         dB, ws, ws_bytes, QLORA_STORE_NF4, stream, nullptr, nullptr);
+}
+
+int qlora_linear_bwd_ex(const uint16_t* dY, const uint16_t* X, const float* T,
+                        const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                        const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                        int32_t r, float scale, uint16_t* dX, float* dA, float* dB, void* ws,
+                        size_t ws_bytes, int32_t store_type, void* stream) {
+  return linear_bwd_impl(dY, X, T, codes, absmax_q, absmax_s2, A, B, M, N, K, r, scale, dX, dA,
+                         dB, ws, ws_bytes, store_type, stream, nullptr, nullptr);
 }
 
 int qlora_dropout_mask(int64_t M, int64_t K, float p, uint64_t seed, uint64_t offset,

@@ -36,21 +36,104 @@ constexpr float round_down_f32(double x) {
   return f;
 }
 
-// Decision thresholds: for a float32 n, "n > kThr[j]" holds exactly when n
-// is strictly closer to level j+1 than to level j, because kThr[j] is the
-// largest float32 not above the exact midpoint. Counting the thresholds that
-// n exceeds therefore gives the nearest level with ties to the lower index.
-struct Thresholds {
-  float t[15];
+
+// FP4 levels (the 4-bit alternative type): the OCP MX E2M1 magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 divided by 6, so the range is [-1, 1] with an
+// exact 0 and exact endpoints; sign-magnitude codes, code 8 s + m is
+// (-1)^s E2M1(m) / 6 (code 8 is -0). Each division is correctly rounded, so
+// each level is the float32 nearest to its exact value.
+constexpr float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+constexpr float fp4_level(int c) { return ((c >> 3) ? -1.0f : 1.0f) * (kE2M1[c & 7] / 6.0f); }
+
+// Store types (bit flags): the level table and the code of the block
+// constants. 0 is NF4 with the 8-bit linear code.
+constexpr int kStoreFP4 = 1;    // FP4 levels instead of NF4
+constexpr int kStoreDqFp8 = 2;  // block constants as E4M3 codes of c / S, S = max / 448
+
+// The levels of a store type in code order, and its constant code.
+struct Codebook {
+  float lv[16];
+  int dq_fp8;
 };
-constexpr Thresholds make_thresholds() {
-  Thresholds r{};
-  for (int j = 0; j < 15; ++j)
-    r.t[j] = round_down_f32((static_cast<double>(kNF4[j]) +
-                             static_cast<double>(kNF4[j + 1])) * 0.5);
+constexpr Codebook make_codebook(int store_type) {
+  Codebook cb{};
+  for (int c = 0; c < 16; ++c) cb.lv[c] = (store_type & kStoreFP4) ? fp4_level(c) : kNF4[c];
+  cb.dq_fp8 = (store_type & kStoreDqFp8) ? 1 : 0;
+  return cb;
+}
+
+// Nearest-level search for quantization: the distinct levels in ascending
+// order (15 for FP4, whose +0 and -0 coincide; 16 for NF4), the decision
+// thresholds between neighbours and the code of each rank. A float32 n
+// takes rank #{j : n > thr[j]}. thr[j] is the largest float32 that goes to
+// the lower level: below the exact midpoint, or at it when a tie goes to
+// the lower level. Ties go, for NF4, to the lower code (its codes are its
+// ranks: the lower level); for FP4, to the code with an even magnitude and
+// then to the lower code (the E2M1 rule, and +0 over -0).
+// Unused thresholds are +inf.
+struct LevelSearch {
+  float thr[15];
+  uint8_t code[16];
+  int nlev;
+};
+constexpr bool code_preferred(int a, int b, bool fp4) {  // a wins a tie against b
+  if (fp4 && (a & 1) != (b & 1)) return (a & 1) == 0;
+  return a < b;
+}
+constexpr float prev_f32(float f) {  // largest float32 below f (f finite, nonzero)
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u = (f > 0.0f) ? u - 1u : u + 1u;
+  return __builtin_bit_cast(float, u);
+}
+constexpr LevelSearch make_level_search(int store_type) {
+  const Codebook cb = make_codebook(store_type);
+  const bool fp4 = (store_type & kStoreFP4) != 0;
+  float lv[16] = {};
+  int cd[16] = {};
+  int n = 0;
+  for (int c = 0; c < 16; ++c) {  // distinct levels, keeping the preferred code
+    int k = 0;
+    while (k < n && lv[k] != cb.lv[c]) ++k;
+    if (k < n) {
+      if (code_preferred(c, cd[k], fp4)) cd[k] = c;
+    } else {
+      lv[n] = cb.lv[c];
+      cd[n] = c;
+      ++n;
+    }
+  }
+  for (int i = 1; i < n; ++i)  // ascending
+    for (int j = i; j > 0 && lv[j - 1] > lv[j]; --j) {
+      const float t = lv[j]; lv[j] = lv[j - 1]; lv[j - 1] = t;
+      const int u = cd[j]; cd[j] = cd[j - 1]; cd[j - 1] = u;
+    }
+  LevelSearch r{};
+  r.nlev = n;
+  for (int j = 0; j < 15; ++j) r.thr[j] = __builtin_huge_valf();
+  for (int j = 0; j + 1 < n; ++j) {
+    const double mid = (static_cast<double>(lv[j]) + static_cast<double>(lv[j + 1])) * 0.5;
+    const float down = round_down_f32(mid);
+    const bool tie_up = !code_preferred(cd[j], cd[j + 1], fp4);
+    r.thr[j] = (tie_up && static_cast<double>(down) == mid) ? prev_f32(down) : down;
+  }
+  for (int j = 0; j < 16; ++j) r.code[j] = (uint8_t)(j < n ? cd[j] : cd[n - 1]);
   return r;
 }
-constexpr Thresholds kThr = make_thresholds();
+
+// NF4: 16 distinct levels whose codes are their ranks, each threshold the
+// largest float32 not above the exact midpoint (ties to the lower level).
+constexpr bool nf4_search_is_plain() {
+  const LevelSearch ls = make_level_search(0);
+  if (ls.nlev != 16) return false;
+  for (int j = 0; j < 16; ++j)
+    if (ls.code[j] != j) return false;
+  for (int j = 0; j < 15; ++j)
+    if (ls.thr[j] != round_down_f32((static_cast<double>(kNF4[j]) + kNF4[j + 1]) * 0.5))
+      return false;
+  return true;
+}
+static_assert(nf4_search_is_plain(), "NF4 level search");
+static_assert(make_level_search(kStoreFP4).nlev == 15, "FP4 has 15 distinct levels");
 
 // ---------------------------------------------------------------------------
 // vector types
@@ -66,14 +149,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
-
-// NF4 level q from immediates (a select chain), without a memory load.
-__device__ __forceinline__ float nf4_level(int q) {
-  float v = kNF4[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) v = (q == i) ? kNF4[i] : v;
-  return v;
 }
 
 // Level lookups for the 8 codes of one dword (element 2j in the low nibble
@@ -118,7 +193,8 @@ __device__ __forceinline__ void packet_levels(const u32x4& c, const float* lv, c
   asm volatile("" ::: "memory");
 }
 
-// Lookups without LDS, for one block constant cs. The 16 possible weights
+// Lookups without LDS, for one block constant cs and the 16 levels lv of
+// the store type (in code order). The 16 possible weights
 // bf16(fl32(L[q] * cs)) are computed once (16 multiplies, the same two
 // roundings as every other path) and split into a low-byte plane and a
 // high-byte plane of 16 bytes each (4 dwords, entry q in byte q % 4 of dword
@@ -128,11 +204,11 @@ __device__ __forceinline__ void packet_levels(const u32x4& c, const float* lv, c
 struct PermTable {
   uint32_t lo[4], hi[4];
 };
-__device__ __forceinline__ PermTable perm_table(float cs) {
+__device__ __forceinline__ PermTable perm_table(float cs, const float (&lv)[16]) {
 #pragma clang fp contract(off)
   uint32_t pk[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pk[i] = pack_bf16x2(kNF4[2 * i] * cs, kNF4[2 * i + 1] * cs);
+  for (int i = 0; i < 8; ++i) pk[i] = pack_bf16x2(lv[2 * i] * cs, lv[2 * i + 1] * cs);
   PermTable t;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -215,12 +291,70 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(v) << 16);
 }
 
+// OCP 8-bit floating-point codes (OFP8; sign, kE exponent bits with bias
+// kBias, kM mantissa bits, subnormals). dec: the value of a code, exactly
+// (the exponent field goes straight into the float's exponent; subnormals
+// are m 2^(1 - bias - kM)).
+template <int kE, int kM, int kBias>
+__device__ __forceinline__ float ofp8_decode(uint32_t c) {
+  const uint32_t s = (c >> 7) & 1u;
+  const uint32_t e = (c >> kM) & ((1u << kE) - 1u);
+  const uint32_t m = c & ((1u << kM) - 1u);
+  const float sub = (float)m * __builtin_bit_cast(float, (uint32_t)(127 + 1 - kBias - kM) << 23);
+  const float nrm = __builtin_bit_cast(float, ((e + 127u - kBias) << 23) | (m << (23 - kM)));
+  const float mag = e ? nrm : sub;
+  return s ? -mag : mag;
+}
+
+// enc for a finite float: the mantissa rounded to kM bits on its integer
+// bits (ties to even), a carry running into the exponent field; values
+// below the smallest normal rounded on the subnormal grid; saturating at
+// kTopCode.
+template <int kE, int kM, int kBias, uint32_t kTopCode>
+__device__ __forceinline__ uint32_t ofp8_encode(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 31) << 7;
+  const uint32_t ua = u & 0x7fffffffu;
+  const float a = __builtin_bit_cast(float, ua);
+  const float top = ofp8_decode<kE, kM, kBias>(kTopCode);
+  const float min_normal = __builtin_bit_cast(float, (uint32_t)(127 + 1 - kBias) << 23);
+  uint32_t mag;
+  if (!(a < top)) {
+    mag = kTopCode;
+  } else if (a < min_normal) {
+    // a 2^(bias - 1 + kM) is exact; rintf rounds half to even
+    mag = (uint32_t)__builtin_rintf(a * __builtin_bit_cast(float, (uint32_t)(127 - 1 + kBias + kM) << 23));
+  } else {
+    const uint32_t e = (ua >> 23) - 127u + kBias;     // biased exponent of the code
+    const uint32_t q = (ua >> (23 - kM)) & ((1u << kM) - 1u);
+    const uint32_t rem = ua & ((1u << (23 - kM)) - 1u);
+    const uint32_t half = 1u << (22 - kM);
+    const uint32_t up = (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+    mag = ((e << kM) + q + up);
+    mag = mag > kTopCode ? kTopCode : mag;
+  }
+  return mag | sign;
+}
+__device__ __forceinline__ float e4m3_decode(uint32_t c) { return ofp8_decode<4, 3, 7>(c); }
+
 // Second-level dequantization of a block constant:
 //   c' = fl32( fl32(q8 / 255) * s2 )   (two separately rounded operations)
 __device__ __forceinline__ float block_scale(uint32_t q8, float s2) {
 #pragma clang fp contract(off)
   const float l8 = static_cast<float>(q8) / 255.0f;  // IEEE division
   return l8 * s2;
+}
+// ... and with the 8-bit floating-point code: c' = fl32(dec(q8) * S)
+// (dec exact), S the group's scale.
+__device__ __forceinline__ float block_scale_fp8(uint32_t q8, float S) {
+#pragma clang fp contract(off)
+  return e4m3_decode(q8) * S;
+}
+// The value of 8-bit constant code k of a store (for the LDS table that the
+// MFMA loaders read): fl32(k / 255), or the E4M3 value.
+__device__ __forceinline__ float level8_of(int k, int dq_fp8) {
+#pragma clang fp contract(off)
+  return dq_fp8 ? e4m3_decode((uint32_t)k) : static_cast<float>(k) / 255.0f;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {

@@ -96,9 +96,10 @@ __device__ __forceinline__ void stage_barrier() {
 // for steps past the end are allowed and harmless.
 
 struct Tables {
-  const float* lv;    // 16 NF4 levels
-  const float* lv16;  // the same levels at a 16-byte stride
-  const float* l8;    // 256 values fl(k / 255)
+  const float* lv;    // 16 levels of the store type (LDS)
+  const float* lv16;  // the same levels at a 16-byte stride (LDS)
+  const float* l8;    // 256 values of the 8-bit constant code (LDS)
+  float klv[16];      // the 16 levels again, wave-uniform (scalar registers)
 };
 
 // Rows of a row-major bf16 matrix, contraction contiguous, moved by direct
@@ -353,7 +354,7 @@ struct Nf4Rows {
     // lookups by v_perm: the forward's consumers are bound by LDS
     // bandwidth, so the producers keep their level lookups out of it
     const int row = t >> 1, half = t & 1;
-    const PermTable pt = perm_table(tb.l8[r.q8] * r.s2);
+    const PermTable pt = perm_table(tb.l8[r.q8] * r.s2, tb.klv);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t a = tile + (uint32_t)tile_off(row, half * 4 + w);
@@ -689,6 +690,15 @@ template <int PT, int QT, class LA1, class LB1, class LA2, class LB2, class Epi>
 struct Contraction {
   LA1 a1; LB1 b1; LA2 a2; LB2 b2; Epi epi;
   int nP, nQ, splits, S1, S2, steps_per_split;
+  // XCD-aware tile order (0: off): workgroup id runs on XCD id % 8, so
+  // workgroups id = x, x + 8, ... take consecutive tiles of an order that
+  // walks groups of xgm P-tiles with q outer; each XCD then covers a block
+  // of about (nP / (nP / xgm)) P-tiles by a share of the Q-tiles, and both
+  // operands are fetched by fewer XCDs. Needs one split, nP*nQ % 8 == 0 and
+  // nP % xgm == 0.
+  int xgm;
+  // levels and 8-bit constant code of a 4-bit weight operand's store type
+  Codebook cb = make_codebook(0);
 };
 
 template <int PT, int QT>
@@ -716,19 +726,26 @@ __device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, 
   // role's barriers are reached only by that role's waves
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  if (tid < 256) {
-#pragma clang fp contract(off)
-    s_l8[tid] = static_cast<float>(tid) / 255.0f;  // IEEE division
-  }
+  if (tid < 256) s_l8[tid] = level8_of(tid, cfg.cb.dq_fp8);
   if (tid < 16) {
-    s_lv[tid] = nf4_level(tid);
-    s_lv16[4 * tid] = nf4_level(tid);
+    s_lv[tid] = cfg.cb.lv[tid];
+    s_lv16[4 * tid] = cfg.cb.lv[tid];
   }
 
   int id = block;
-  const int pt = id % cfg.nP; id /= cfg.nP;
-  const int qt = id % cfg.nQ; id /= cfg.nQ;
-  const int split = id;
+  int pt, qt, split;
+  if (cfg.xgm > 0) {
+    const int tiles = cfg.nP * cfg.nQ;
+    const int L = (id & 7) * (tiles >> 3) + (id >> 3);
+    const int grp = cfg.xgm * cfg.nQ;
+    pt = (L / grp) * cfg.xgm + L % cfg.xgm;
+    qt = (L % grp) / cfg.xgm;
+    split = 0;
+  } else {
+    pt = id % cfg.nP; id /= cfg.nP;
+    qt = id % cfg.nQ; id /= cfg.nQ;
+    split = id;
+  }
   const int total = cfg.S1 + cfg.S2;
   const int s_begin = split * cfg.steps_per_split;
   const int s_end = min(total, s_begin + cfg.steps_per_split);
@@ -816,7 +833,9 @@ __device__ __forceinline__ void contraction_body(const Contraction<PT, QT, LA1, 
 
   // ---- producers: exactly n barriers, one after each produced step ----
   const int t = tid - kCW * 64;
-  const Tables tb{s_lv, s_lv16, s_l8};
+  Tables tb{s_lv, s_lv16, s_l8, {}};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tb.klv[i] = cfg.cb.lv[i];
 
   LA2 a2 = cfg.a2; LB2 b2 = cfg.b2;
   auto seg2_step = [&](int s) {  // local step s >= n1, loaded synchronously

@@ -127,6 +127,7 @@ struct GemvArgs {
   float scale;
   uint16_t* Y;
   float* T_out;    // optional
+  Codebook cb;     // levels and constant code of the store type
 };
 
 // kMX: the largest M the instantiation serves (4 or 16: the token rows a
@@ -239,8 +240,9 @@ __global__ void __launch_bounds__(kThreads) nf4_gemv_kernel(GemvArgs a) {
 
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      const float cs = kDQ ? block_scale(q8[st], s2[st]) : s2[st];
-      const PermTable pt = perm_table(cs);  // lookups by v_perm: no LDS round trips
+      const float cs = !kDQ ? s2[st]
+                       : a.cb.dq_fp8 ? block_scale_fp8(q8[st], s2[st]) : block_scale(q8[st], s2[st]);
+      const PermTable pt = perm_table(cs, a.cb.lv);  // lookups by v_perm: no LDS round trips
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         // MFMA t takes this lane's codes 8 t .. 8 t + 7 and the same k of the
@@ -370,7 +372,7 @@ hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemvArgs a{X, W.codes, W.absmax_q, W.absmax_s2, B, M, r, N, K, tchunks, part_t, scale, Y,
-             T_out};
+             T_out, codebook_of(W)};
   const size_t lds = gemv_lds_bytes(M, r);
   e = record_if(ev0, stream);
   if (e != hipSuccess) return e;

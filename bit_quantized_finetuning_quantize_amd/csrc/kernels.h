@@ -7,25 +7,34 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace qlora {
 
 struct Nf4Weight {
   const uint8_t* codes;
   const uint8_t* absmax_q;
   const float* absmax_s2;
+  int store_type = 0;  // kStoreFP4 | kStoreDqFp8 (common.h); 0 is NF4, linear code
 };
 
+// The level table and constant code the kernels use for a store. A store
+// without double quantization keeps float32 constants, so the constant code
+// does not apply (the loaders read it with the 8-bit code forced to 255,
+// whose linear value is exactly 1).
+inline Codebook codebook_of(const Nf4Weight& W) {
+  return make_codebook(W.absmax_q ? W.store_type : (W.store_type & kStoreFP4));
+}
+
 hipError_t launch_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
-                               uint8_t* absmax_q, float* absmax_s2,
+                               uint8_t* absmax_q, float* absmax_s2, int store_type,
                                hipStream_t stream);
 
-hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
-                                 const float* absmax_s2, int64_t numel, void* out,
-                                 bool bf16, hipStream_t stream);
+hipError_t launch_nf4_dequantize(Nf4Weight W, int64_t numel, void* out, bool bf16,
+                                 hipStream_t stream);
 
 // Merged 16-bit weight: bf16(w' + s (A B)^T), [N x K] row-major.
-hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q,
-                            const float* absmax_s2, int64_t N, int64_t K, const uint16_t* A,
+hipError_t launch_nf4_merge(Nf4Weight W, int64_t N, int64_t K, const uint16_t* A,
                             const uint16_t* B, int r, float scale, uint16_t* out,
                             hipStream_t stream);
 

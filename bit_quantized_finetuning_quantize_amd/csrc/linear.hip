@@ -290,6 +290,16 @@ hipError_t run_pair(Contraction<PT, QT, LA1, LB1, LA2, LB2, Epi> c0,
   return hipGetLastError();
 }
 
+// XCD-aware tile order for a one-split launch: groups of half the P-tiles
+// (each XCD then takes about half the P-tiles and a quarter of the Q-tiles),
+// when the tile count divides among the 8 XCDs.
+template <class C>
+void set_xcd_order(C& cfg) {
+  cfg.xgm = 0;
+  if (cfg.splits == 1 && ((int64_t)cfg.nP * cfg.nQ) % 8 == 0 && cfg.nP % 2 == 0)
+    cfg.xgm = cfg.nP / 2;
+}
+
 template <class C>
 void set_steps(C& cfg, int64_t S1, int64_t S2, int64_t tiles) {
   cfg.S1 = (int)S1;
@@ -410,6 +420,8 @@ hipError_t launch_fwd_gemm(const uint16_t* X, Nf4Weight W, const uint16_t* A,
   cfg.splits = 1;
   cfg.steps_per_split = cfg.S1 + cfg.S2;
   cfg.epi = EpiBf16{Y, N, M, N};
+  cfg.cb = codebook_of(W);
+  set_xcd_order(cfg);
   QLORA_TRY(record_if(ev0, stream));
   QLORA_TRY((run<256, 128, LA1, LB1, LA2, LB2, EpiBf16, false>(cfg, stream)));
   return record_if(ev1, stream);
@@ -440,6 +452,8 @@ hipError_t input_grad(const uint16_t* dY, Nf4Weight W, const uint16_t* apad, int
   cfg.splits = 1;
   cfg.steps_per_split = cfg.S1 + cfg.S2;
   cfg.epi = epi;
+  cfg.cb = codebook_of(W);
+  set_xcd_order(cfg);
   if (Epi::kKeepSeg2 && cfg.S2 > 3) return hipErrorInvalidValue;  // rejected by the API
   return run<256, 128, LA1, LB1, LA2, LB2, Epi, false>(cfg, stream);
 }

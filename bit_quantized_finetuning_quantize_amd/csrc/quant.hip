@@ -25,31 +25,40 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kRounds = kGroup * kBlock / (kQuantThreads * 8);  // 8
 
-// The nearest level's index q = #{j : n > thr[j]}, found by a four-step
+// The nearest level's rank q = #{j : n > thr[j]}, found by a four-step
 // binary search over the 15 sorted thresholds: thr holds them in LDS (its
 // 15 entries sit on 15 different banks, so the lane-varying reads do not
 // conflict). Equal to counting for every n, NaN included (every comparison
 // is false, q = 0).
-__device__ __forceinline__ uint32_t nf4_index(float n, const float* thr) {
-  uint32_t q = (n > kThr.t[7]) ? 8u : 0u;
+template <bool kFP4>
+__device__ __forceinline__ uint32_t level_rank(float n, const float* thr) {
+  constexpr LevelSearch kLS = make_level_search(kFP4 ? kStoreFP4 : 0);
+  uint32_t q = (n > kLS.thr[7]) ? 8u : 0u;
   q += (n > thr[q + 3]) ? 4u : 0u;
   q += (n > thr[q + 1]) ? 2u : 0u;
   q += (n > thr[q]) ? 1u : 0u;
   return q;
 }
 
-template <bool kVec>
+// kFP4: FP4 levels (ranks map to sign-magnitude codes through an LDS table);
+// else NF4 (the code is the rank). dq_fp8: the block constants as E4M3
+// codes of c / S with S = fl(max / 448) per group (else the linear code).
+template <bool kVec, bool kFP4>
 __global__ void __launch_bounds__(kQuantThreads)
 nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
                     uint8_t* __restrict__ codes, uint8_t* __restrict__ absmax_q,
-                    float* __restrict__ absmax_s2) {
+                    float* __restrict__ absmax_s2, int dq_fp8) {
 #pragma clang fp contract(off)
+  constexpr LevelSearch kLS = make_level_search(kFP4 ? kStoreFP4 : 0);
+  constexpr uint32_t kZeroCode = kFP4 ? 0u : 7u;  // the code of level 0
   __shared__ float s_blockmax[kGroup];
   __shared__ float s_wavemax[kQuantThreads / 64];
   __shared__ float s_thr[16];
+  __shared__ uint32_t s_code[16];
 
   const int tid = threadIdx.x;
-  if (tid < 15) s_thr[tid] = kThr.t[tid];  // visible after the first barrier
+  if (tid < 15) s_thr[tid] = kLS.thr[tid];  // visible after the first barrier
+  if (tid < 16) s_code[tid] = kLS.code[tid];
   const int64_t group = blockIdx.x;
   const int64_t gbase = group * (int64_t)(kGroup * kBlock);
   const int64_t nbytes = (numel + 1) / 2;
@@ -96,7 +105,17 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
                          fmaxf(s_wavemax[2], s_wavemax[3]));
 
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
-  if (absmax_q) {
+  if (absmax_q && dq_fp8) {
+    // 8-bit floating-point constant code: S = fl(max / 448), q8 = E4M3 of
+    // fl(c / S) (nearest, ties to even, saturating at 448)
+    const float S = s2 / 448.0f;  // IEEE division
+    const int64_t b = group * kGroup + tid;
+    if (b < nblocks) {
+      const uint32_t q8 = S > 0.0f ? ofp8_encode<4, 3, 7, 0x7Eu>(s_blockmax[tid] / S) : 0u;
+      absmax_q[b] = (uint8_t)q8;
+    }
+    if (tid == 0) absmax_s2[group] = S;
+  } else if (absmax_q) {
     const int64_t b = group * kGroup + tid;
     if (b < nblocks) {
       uint32_t q8 = 0;
@@ -125,8 +144,10 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
     // pair |w| <= c (checked exhaustively on gfx950: 1,065,402,238 pairs, no
     // difference inside that range, differences only beyond it, where the
     // reciprocal leaves the normal range); outside it the IEEE division.
+    // (the reciprocal was checked against the NF4 thresholds only: FP4
+    // divides)
     float n[8];
-    if (c >= 0x1p-100f && c <= 0x1p100f) {
+    if (!kFP4 && c >= 0x1p-100f && c <= 0x1p100f) {
       const float rc = __builtin_amdgcn_rcpf(c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -143,8 +164,12 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t qa = (c > 0.0f) ? nf4_index(n[2 * i], s_thr) : 7u;
-      uint32_t qb = (c > 0.0f) ? nf4_index(n[2 * i + 1], s_thr) : 7u;
+      uint32_t qa = (c > 0.0f) ? level_rank<kFP4>(n[2 * i], s_thr) : kZeroCode;
+      uint32_t qb = (c > 0.0f) ? level_rank<kFP4>(n[2 * i + 1], s_thr) : kZeroCode;
+      if (kFP4 && c > 0.0f) {
+        qa = s_code[qa];
+        qb = s_code[qb];
+      }
       // nibbles past the end of the tensor stay 0
       if (e0 + 2 * i >= numel) qa = 0u;
       if (e0 + 2 * i + 1 >= numel) qb = 0u;
@@ -168,10 +193,10 @@ __global__ void __launch_bounds__(256)
 nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
                       const uint8_t* __restrict__ absmax_q,
                       const float* __restrict__ absmax_s2, int64_t numel,
-                      void* __restrict__ out) {
+                      void* __restrict__ out, Codebook cb) {
 #pragma clang fp contract(off)
   __shared__ float s_lv[16];
-  if (threadIdx.x < 16) s_lv[threadIdx.x] = kNF4[threadIdx.x];
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = cb.lv[threadIdx.x];
   __syncthreads();
   const int64_t nwords = (numel + 7) / 8;
   const int64_t nbytes = (numel + 1) / 2;
@@ -191,7 +216,9 @@ nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
         if (i * 4 + j < nbytes) word |= (uint32_t)codes[i * 4 + j] << (8 * j);
     }
     const int64_t b = e0 / kBlock;
-    const float cs = absmax_q ? block_scale(absmax_q[b], absmax_s2[b / kGroup]) : absmax_s2[b];
+    const float cs = !absmax_q ? absmax_s2[b]
+                     : cb.dq_fp8 ? block_scale_fp8(absmax_q[b], absmax_s2[b / kGroup])
+                                 : block_scale(absmax_q[b], absmax_s2[b / kGroup]);
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = s_lv[(word >> (4 * j)) & 15u] * cs;
@@ -227,17 +254,25 @@ nf4_dequantize_kernel(const uint8_t* __restrict__ codes,
 }  // namespace
 
 hipError_t launch_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
-                               uint8_t* absmax_q, float* absmax_s2,
+                               uint8_t* absmax_q, float* absmax_s2, int store_type,
                                hipStream_t stream) {
   const int64_t ngroups = (numel + (int64_t)kGroup * kBlock - 1) / ((int64_t)kGroup * kBlock);
   const bool vec = (reinterpret_cast<uintptr_t>(w) % 16) == 0;
+  const bool fp4 = (store_type & kStoreFP4) != 0;
+  const int dq_fp8 = (store_type & kStoreDqFp8) ? 1 : 0;
   dim3 grid((unsigned)ngroups), block(kQuantThreads);
-  if (vec)
-    hipLaunchKernelGGL(nf4_quantize_kernel<true>, grid, block, 0, stream, w, numel,
-                       codes, absmax_q, absmax_s2);
+  if (vec && !fp4)
+    hipLaunchKernelGGL((nf4_quantize_kernel<true, false>), grid, block, 0, stream, w, numel,
+                       codes, absmax_q, absmax_s2, dq_fp8);
+  else if (!fp4)
+    hipLaunchKernelGGL((nf4_quantize_kernel<false, false>), grid, block, 0, stream, w, numel,
+                       codes, absmax_q, absmax_s2, dq_fp8);
+  else if (vec)
+    hipLaunchKernelGGL((nf4_quantize_kernel<true, true>), grid, block, 0, stream, w, numel,
+                       codes, absmax_q, absmax_s2, dq_fp8);
   else
-    hipLaunchKernelGGL(nf4_quantize_kernel<false>, grid, block, 0, stream, w, numel,
-                       codes, absmax_q, absmax_s2);
+    hipLaunchKernelGGL((nf4_quantize_kernel<false, true>), grid, block, 0, stream, w, numel,
+                       codes, absmax_q, absmax_s2, dq_fp8);
   return hipGetLastError();
 }
 
@@ -257,7 +292,7 @@ __global__ void __launch_bounds__(256)
 nf4_merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
                  const float* __restrict__ absmax_s2, int64_t N, int64_t K,
                  const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r,
-                 float s, uint16_t* __restrict__ out) {
+                 float s, uint16_t* __restrict__ out, Codebook cb) {
 #pragma clang fp contract(off)
   __shared__ float s_lv[16];
   __shared__ __attribute__((aligned(16))) float s_at[kMergeRC][64];  // A[k0 + k][j0 + j]
@@ -266,7 +301,7 @@ nf4_merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
   const int rp = tid >> 3, cr = tid & 7;
   const int64_t k = k0 + 8 * cr;
-  if (tid < 16) s_lv[tid] = kNF4[tid];
+  if (tid < 16) s_lv[tid] = cb.lv[tid];
 
   float acc[2][8];
 #pragma unroll
@@ -305,7 +340,9 @@ nf4_merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
     const int64_t e0 = n * K + k;                       // first of 8 elements, one block
     const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
     const int64_t b = e0 / kBlock;
-    const float cs = absmax_q ? block_scale(absmax_q[b], absmax_s2[b / kGroup]) : absmax_s2[b];
+    const float cs = !absmax_q ? absmax_s2[b]
+                     : cb.dq_fp8 ? block_scale_fp8(absmax_q[b], absmax_s2[b / kGroup])
+                                 : block_scale(absmax_q[b], absmax_s2[b / kGroup]);
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -318,28 +355,26 @@ nf4_merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
   }
 }
 
-hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q,
-                            const float* absmax_s2, int64_t N, int64_t K, const uint16_t* A,
+hipError_t launch_nf4_merge(Nf4Weight W, int64_t N, int64_t K, const uint16_t* A,
                             const uint16_t* B, int r, float scale, uint16_t* out,
                             hipStream_t stream) {
   dim3 grid((unsigned)(K / 64), (unsigned)((N + 63) / 64));
-  hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), 0, stream, codes, absmax_q, absmax_s2, N,
-                     K, A, B, r, scale, out);
+  hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), 0, stream, W.codes, W.absmax_q,
+                     W.absmax_s2, N, K, A, B, r, scale, out, codebook_of(W));
   return hipGetLastError();
 }
 
-hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
-                                 const float* absmax_s2, int64_t numel, void* out,
-                                 bool bf16, hipStream_t stream) {
+hipError_t launch_nf4_dequantize(Nf4Weight W, int64_t numel, void* out, bool bf16,
+                                 hipStream_t stream) {
   const int64_t nwords = (numel + 7) / 8;
   int64_t blocks = (nwords + 511) / 512;  // two words per thread
   if (blocks > 65536) blocks = 65536;
   if (bf16)
     hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, codes, absmax_q, absmax_s2, numel, out);
+                       stream, W.codes, W.absmax_q, W.absmax_s2, numel, out, codebook_of(W));
   else
     hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, codes, absmax_q, absmax_s2, numel, out);
+                       stream, W.codes, W.absmax_q, W.absmax_s2, numel, out, codebook_of(W));
   return hipGetLastError();
 }
 

@@ -64,6 +64,26 @@
  *             the float32 constant (largest magnitude) of each block,
  * so that c' = absmax_s2[b]. The codes are the same in both stores. Every
  * entry point that takes a store accepts either form.
+ *
+ * Store types (the _ex entry points; bit flags, 0 everywhere else)
+ * ----------------------------------------------------------------
+ * QLORA_STORE_FP4: the levels are FP4 instead of NF4 (the 4-bit alternative
+ *   that ozercemkelahmet.com "QLoRA", Common mistakes, warns not to pick
+ *   without a reason; the pages do not define it): the OCP MX E2M1
+ *   magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 divided by 6, sign-magnitude codes
+ *   (code 8 s + m is (-1)^s E2M1(m) / 6, each level the nearest float32),
+ *   so the range is [-1, 1] with an exact 0. A value takes the code of the
+ *   nearest level; of two equally near, the one with an even magnitude m,
+ *   then the lower code (0 goes to code 0); an all-zero block stores code 0.
+ * QLORA_STORE_DQ_FP8: the 8-bit code of the block constants is the OCP E4M3
+ *   code relative to a per-group scale instead of the linear code
+ *   (ozercemkelahmet.com "QLoRA", Step 3 says 8 bits, not which code):
+ *     S = fl32(max c / 448),  absmax_q[b] = E4M3(fl32(c / S)) (nearest,
+ *     ties to even, saturating at 448; 0 when S = 0),  absmax_s2[g] = S,
+ *     c' = fl32(dec(absmax_q[b]) * S).
+ *   With absmax_q = NULL (no double quantization) this flag has no effect.
+ * Buffers and sizes are the same for every type; w' = fl32(L[code] * c')
+ * with L the type's levels in code order.
  */
 #ifndef QLORA_H
 #define QLORA_H
@@ -83,6 +103,10 @@ enum {
   QLORA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   QLORA_ERR_HIP = -4          /* a HIP launch failed; see qlora_last_hip_error() */
 };
+
+#define QLORA_STORE_NF4 0
+#define QLORA_STORE_FP4 1
+#define QLORA_STORE_DQ_FP8 2
 
 #define QLORA_NF4_BLOCK 64
 #define QLORA_NF4_GROUP 256
@@ -130,6 +154,14 @@ void qlora_nf4_codebook(float* levels);
 int qlora_nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_s2, void* stream);
 
+/* qlora_nf4_quantize_ex — qlora_nf4_quantize for any store type (see
+ * "Store types"); store_type 0 is qlora_nf4_quantize.
+ * Errors: as qlora_nf4_quantize; INVALID_ARG for a store_type outside
+ * [0, 3]. */
+int qlora_nf4_quantize_ex(const uint16_t* w, int64_t numel, uint8_t* codes,
+                          uint8_t* absmax_q, float* absmax_s2, int32_t store_type,
+                          void* stream);
+
 /* qlora_nf4_dequantize — expand a store to float32 w' (the formula in
  * "The NF4 store"; ozercemkelahmet.com "QLoRA", "A worked example" step 4).
  *   out        device, float [numel]
@@ -146,6 +178,15 @@ int qlora_nf4_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
 int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
                               const float* absmax_s2, int64_t numel,
                               uint16_t* out, void* stream);
+
+/* The two dequantizations for any store type (store_type before the
+ * output); errors as above, INVALID_ARG for a store_type outside [0, 3]. */
+int qlora_nf4_dequantize_ex(const uint8_t* codes, const uint8_t* absmax_q,
+                            const float* absmax_s2, int64_t numel, int32_t store_type,
+                            float* out, void* stream);
+int qlora_nf4_dequantize_bf16_ex(const uint8_t* codes, const uint8_t* absmax_q,
+                                 const float* absmax_s2, int64_t numel, int32_t store_type,
+                                 uint16_t* out, void* stream);
 
 /* qlora_nf4_merge — the adapter folded into a 16-bit copy of the frozen
  * weight (ozercemkelahmet.com "QLoRA", How it works, Step 8: save and use:
@@ -166,6 +207,10 @@ int qlora_nf4_dequantize_bf16(const uint8_t* codes, const uint8_t* absmax_q,
 int qlora_nf4_merge(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
                     int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
                     float scale, uint16_t* out, void* stream);
+/* ... for any store type (INVALID_ARG for a store_type outside [0, 3]). */
+int qlora_nf4_merge_ex(const uint8_t* codes, const uint8_t* absmax_q, const float* absmax_s2,
+                       int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int32_t r,
+                       float scale, int32_t store_type, uint16_t* out, void* stream);
 
 /* qlora_adamw_step — one AdamW step for adapter parameters, in place
  * (ozercemkelahmet.com "QLoRA", "Practical guidance and best practices",
@@ -265,6 +310,16 @@ int qlora_linear_fwd(const uint16_t* X, const uint8_t* codes,
                      uint16_t* Y, float* T_out, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* qlora_linear_fwd_ex — qlora_linear_fwd on a store of any type (the GEMV
+ * and the MFMA path take the type's levels and constant code); errors as
+ * qlora_linear_fwd, INVALID_ARG for a store_type outside [0, 3]. */
+int qlora_linear_fwd_ex(const uint16_t* X, const uint8_t* codes,
+                        const uint8_t* absmax_q, const float* absmax_s2,
+                        const uint16_t* A, const uint16_t* B, int64_t M,
+                        int64_t N, int64_t K, int32_t r, float scale,
+                        uint16_t* Y, float* T_out, void* ws, size_t ws_bytes,
+                        int32_t store_type, void* stream);
+
 /* qlora_linear_bwd — gradients through the dequantized frozen weight into
  * the input and the adapter; no gradient for the 4-bit weight
  * (ozercemkelahmet.com "QLoRA", Step 6; crackai.dev "QLoRA: Efficient
@@ -309,6 +364,16 @@ int qlora_linear_fwd_noalloc(const uint16_t* X, const uint8_t* codes,
                              const uint16_t* A, const uint16_t* B, int64_t M,
                              int64_t N, int64_t K, int32_t r, float scale,
                              uint16_t* Y, float* T_out, void* stream);
+
+/* qlora_linear_bwd_ex — qlora_linear_bwd on a store of any type; errors as
+ * qlora_linear_bwd, INVALID_ARG for a store_type outside [0, 3]. */
+int qlora_linear_bwd_ex(const uint16_t* dY, const uint16_t* X, const float* T,
+                        const uint8_t* codes, const uint8_t* absmax_q,
+                        const float* absmax_s2, const uint16_t* A,
+                        const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                        int32_t r, float scale, uint16_t* dX, float* dA,
+                        float* dB, void* ws, size_t ws_bytes, int32_t store_type,
+                        void* stream);
 
 /* ---- profiling variants ------------------------------------------------------
  * Identical to qlora_linear_fwd / qlora_linear_bwd, and in addition record

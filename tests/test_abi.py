@@ -145,6 +145,31 @@ def test_linear_fwd_noalloc_rejects(lib):
         assert 0 < lib.qlora_linear_workspace_bytes(M, N, K, r) <= NOALLOC_SCRATCH_BYTES
 
 
+def test_store_type_rejected_outside_range(lib):
+    """Every _ex entry point rejects a store type outside [0, 3] before any
+    GPU call."""
+    for t in (-1, 4, 1 << 20):
+        assert lib.qlora_nf4_quantize_ex(FAKE, 64, FAKE, FAKE, FAKE, t, None) == -1
+        assert lib.qlora_nf4_dequantize_ex(FAKE, FAKE, FAKE, 64, t, FAKE, None) == -1
+        assert lib.qlora_nf4_dequantize_bf16_ex(FAKE, FAKE, FAKE, 64, t, FAKE, None) == -1
+        assert lib.qlora_nf4_merge_ex(FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 1.0, t, FAKE,
+                                      None) == -1
+        assert lib.qlora_linear_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128, 128, 8, 1.0,
+                                       FAKE, None, FAKE, 1 << 30, t, None) == -1
+        assert lib.qlora_linear_bwd_ex(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128,
+                                       128, 8, 1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, t,
+                                       None) == -1
+    # a valid type passes validation up to the first shape check
+    assert lib.qlora_linear_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128, 100, 8, 1.0,
+                                   FAKE, None, FAKE, 1 << 30, 3, None) == -2
+
+
+def test_header_store_type_values():
+    text = open(HEADER).read()
+    for name, v in (("QLORA_STORE_NF4", 0), ("QLORA_STORE_FP4", 1), ("QLORA_STORE_DQ_FP8", 2)):
+        assert re.search(rf"#define {name} {v}\b", text), name
+
+
 def test_linear_bwd_rejects(lib):
     b = lib.qlora_linear_bwd
     args = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 128, 128, 8, 1.0, FAKE, FAKE,
