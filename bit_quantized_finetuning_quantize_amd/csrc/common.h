@@ -120,6 +120,59 @@ constexpr LevelSearch make_level_search(int store_type) {
   return r;
 }
 
+// The same search by bins, one table entry per value: bin b holds the n with
+// (n + 1) * 15 in [b, b + 1), b = 0 .. 31 (n below -1 clamped into bin 0,
+// above 1 into the last bins). Each bin holds at most one threshold; its
+// entry is that threshold (+inf if none) and the codes below and above it.
+// Since no threshold lies near a bin edge (bin_search_ok), a bin index that
+// the rounding of (n + 1) * 15 moves across an edge selects the same code.
+constexpr int kBins = 32;
+struct BinSearch {
+  float thr[kBins];
+  uint32_t codes[kBins];  // code below the threshold (bits 0-15), above it (bits 16-31)
+};
+constexpr BinSearch make_bin_search(int store_type) {
+  const LevelSearch ls = make_level_search(store_type);
+  BinSearch b{};
+  for (int k = 0; k < kBins; ++k) {
+    const double lo = k / 15.0 - 1.0, hi = (k + 1) / 15.0 - 1.0;
+    int base = 0;
+    float t = __builtin_huge_valf();
+    for (int j = 0; j < 15; ++j) {
+      const double tj = static_cast<double>(ls.thr[j]);
+      if (tj < lo) ++base;
+      else if (tj < hi) t = ls.thr[j];
+    }
+    b.thr[k] = t;
+    b.codes[k] = (uint32_t)ls.code[base] | ((uint32_t)ls.code[base < 15 ? base + 1 : 15] << 16);
+  }
+  return b;
+}
+// At most one threshold per bin, and every threshold at least 1/1000 of a
+// bin away from a bin edge (the rounding of (n + 1) * 15 is below 2^-19).
+constexpr bool bin_search_ok(int store_type) {
+  const LevelSearch ls = make_level_search(store_type);
+  for (int k = 0; k < kBins; ++k) {
+    const double lo = k / 15.0 - 1.0, hi = (k + 1) / 15.0 - 1.0;
+    int cnt = 0;
+    for (int j = 0; j < 15; ++j) {
+      const double tj = static_cast<double>(ls.thr[j]);
+      if (tj >= lo && tj < hi) ++cnt;
+    }
+    if (cnt > 1) return false;
+  }
+  for (int j = 0; j < 15; ++j) {
+    const double tj = static_cast<double>(ls.thr[j]);
+    if (tj > 1.0) continue;  // unused (+inf)
+    const double x = (tj + 1.0) * 15.0;
+    const double f = x - static_cast<double>(static_cast<int64_t>(x));
+    if (f < 1e-3 || f > 1.0 - 1e-3) return false;
+  }
+  return true;
+}
+static_assert(bin_search_ok(0), "NF4 thresholds fit the bins");
+static_assert(bin_search_ok(kStoreFP4), "FP4 thresholds fit the bins");
+
 // NF4: 16 distinct levels whose codes are their ranks, each threshold the
 // largest float32 not above the exact midpoint (ties to the lower level).
 constexpr bool nf4_search_is_plain() {

@@ -9,12 +9,16 @@
 // group of 256 blocks); ai360xpert.com "QLoRA", How It Works item 2 (the
 // per-block constants shrink from 32 to 8 bits).
 //
-// Layout of one launch: one workgroup per group of 256 blocks (16384 values).
-// Within a workgroup, eight consecutive lanes own one block (8 values each,
-// one 16-byte load), so every load instruction of a wave reads 1 KiB of
-// contiguous HBM and a block maximum is a three-step xor shuffle. A
-// workgroup walks its group in 8 rounds of 32 blocks, keeping the values in
-// registers, so each input byte is read once.
+// Layout of one launch: one workgroup of 512 lanes per group of 256 blocks
+// (16384 values). Within a workgroup, eight consecutive lanes own one block
+// (8 values each, one 16-byte load), so every load instruction of a wave
+// reads 1 KiB of contiguous HBM and a block maximum is three DPP steps. A
+// workgroup loads its group in 4 rounds of 64 blocks, all loads issued before
+// the first reduction, and keeps the values in registers, so each input byte
+// is read once. The nearest level is found without a search: n maps to one
+// of 32 bins of width 1/15 on [-1, 1], and each bin holds at most one
+// threshold between levels, so one table read and one comparison give the
+// code.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,50 +26,60 @@ namespace qlora {
 
 namespace {
 
-constexpr int kQuantThreads = 256;
-constexpr int kRounds = kGroup * kBlock / (kQuantThreads * 8);  // 8
+#ifndef QUANT_THREADS
+#define QUANT_THREADS 512
+#endif
+constexpr int kQuantThreads = QUANT_THREADS;
+constexpr int kRounds = kGroup * kBlock / (kQuantThreads * 8);
+static_assert(kQuantThreads >= kGroup && kRounds >= 1, "one thread per block constant");
 
-// The nearest level's rank q = #{j : n > thr[j]}, found by a four-step
-// binary search over the 15 sorted thresholds: thr holds them in LDS (its
-// 15 entries sit on 15 different banks, so the lane-varying reads do not
-// conflict). Equal to counting for every n, NaN included (every comparison
-// is false, q = 0).
+// The code of the nearest level of n: one entry of the bin table (LDS,
+// 8 bytes per bin: the bin's threshold and the codes below and above it;
+// NF4 keeps only the code below, as the code above is the next one).
+// NaN, which every threshold comparison leaves at rank 0, lands in bin 0 by
+// the clamp (maxNum), where n > thr is false: the code of rank 0, as the
+// threshold count gives it. Values beyond +-1 clamp into the outer bins.
 template <bool kFP4>
-__device__ __forceinline__ uint32_t level_rank(float n, const float* thr) {
-  constexpr LevelSearch kLS = make_level_search(kFP4 ? kStoreFP4 : 0);
-  uint32_t q = (n > kLS.thr[7]) ? 8u : 0u;
-  q += (n > thr[q + 3]) ? 4u : 0u;
-  q += (n > thr[q + 1]) ? 2u : 0u;
-  q += (n > thr[q]) ? 1u : 0u;
-  return q;
+__device__ __forceinline__ uint32_t bin_code(float n, const u32x2* bins) {
+  const float x = fminf(fmaxf(__builtin_fmaf(n, 15.0f, 15.0f), 0.0f), (float)(kBins - 1));
+  const u32x2 e = bins[(int)x];
+  const bool above = n > __builtin_bit_cast(float, e.x);
+  if constexpr (kFP4) return (e.y >> (above ? 16u : 0u)) & 0xfu;
+  return e.y + (above ? 1u : 0u);
 }
 
-// kFP4: FP4 levels (ranks map to sign-magnitude codes through an LDS table);
-// else NF4 (the code is the rank). dq_fp8: the block constants as E4M3
-// codes of c / S with S = fl(max / 448) per group (else the linear code).
+// A lane's value from another lane of its row, by a DPP control word.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// kFP4: FP4 levels (sign-magnitude codes); else NF4 (the code is the rank).
+// dq_fp8: the block constants as E4M3 codes of c / S with S = fl(max / 448)
+// per group (else the linear code).
 template <bool kVec, bool kFP4>
 __global__ void __launch_bounds__(kQuantThreads)
 nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
                     uint8_t* __restrict__ codes, uint8_t* __restrict__ absmax_q,
                     float* __restrict__ absmax_s2, int dq_fp8) {
 #pragma clang fp contract(off)
-  constexpr LevelSearch kLS = make_level_search(kFP4 ? kStoreFP4 : 0);
+  constexpr BinSearch kBS = make_bin_search(kFP4 ? kStoreFP4 : 0);
   constexpr uint32_t kZeroCode = kFP4 ? 0u : 7u;  // the code of level 0
   __shared__ float s_blockmax[kGroup];
   __shared__ float s_wavemax[kQuantThreads / 64];
-  __shared__ float s_thr[16];
-  __shared__ uint32_t s_code[16];
+  __shared__ u32x2 s_bins[kBins];
 
   const int tid = threadIdx.x;
-  if (tid < 15) s_thr[tid] = kLS.thr[tid];  // visible after the first barrier
-  if (tid < 16) s_code[tid] = kLS.code[tid];
+  if (tid < kBins)  // visible after the first barrier
+    s_bins[tid] = u32x2{__builtin_bit_cast(uint32_t, kBS.thr[tid]),
+                        kFP4 ? kBS.codes[tid] : (kBS.codes[tid] & 0xFFFFu)};
+  const int64_t nbytes = (numel + 1) / 2;
+  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
   const int64_t group = blockIdx.x;
   const int64_t gbase = group * (int64_t)(kGroup * kBlock);
-  const int64_t nbytes = (numel + 1) / 2;
 
-  uint32_t vals[kRounds][4];  // 8 bf16 per round
-  float cmax[kRounds];
-
+  uint32_t vals[kRounds][4];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int64_t e0 = gbase + (int64_t)r * (kQuantThreads * 8) + tid * 8;
@@ -80,44 +94,50 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
       for (int i = 0; i < 4; ++i)
         vals[r][i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
     }
+  }
+
+  float cmax[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       m = fmaxf(m, fabsf(bf16_lo(vals[r][i])));
       m = fmaxf(m, fabsf(bf16_hi(vals[r][i])));
     }
-    // the 8 lanes of a block are consecutive and aligned to 8 inside a wave
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
+    // the 8 lanes of a block are consecutive and aligned to 8 inside a
+    // wave: swap neighbours, then pairs (quad permutations), then mirror
+    // each half-row of 8 lanes, which pairs the two quads of a block
+    m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1,0,3,2]
+    m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2,3,0,1]
+    m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
     cmax[r] = m;
     if ((tid & 7) == 0) s_blockmax[r * (kQuantThreads / 8) + tid / 8] = m;
   }
   __syncthreads();
 
   // second level: group maximum over the 256 block constants
-  float gm = s_blockmax[tid];
+  float gm = tid < kGroup ? s_blockmax[tid] : 0.0f;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
   if ((tid & 63) == 0) s_wavemax[tid / 64] = gm;
   __syncthreads();
-  const float s2 = fmaxf(fmaxf(s_wavemax[0], s_wavemax[1]),
-                         fmaxf(s_wavemax[2], s_wavemax[3]));
+  float s2 = s_wavemax[0];
+#pragma unroll
+  for (int i = 1; i < kQuantThreads / 64; ++i) s2 = fmaxf(s2, s_wavemax[i]);
 
-  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
+  const int64_t b = group * kGroup + tid;
   if (absmax_q && dq_fp8) {
     // 8-bit floating-point constant code: S = fl(max / 448), q8 = E4M3 of
     // fl(c / S) (nearest, ties to even, saturating at 448)
     const float S = s2 / 448.0f;  // IEEE division
-    const int64_t b = group * kGroup + tid;
-    if (b < nblocks) {
+    if (tid < kGroup && b < nblocks) {
       const uint32_t q8 = S > 0.0f ? ofp8_encode<4, 3, 7, 0x7Eu>(s_blockmax[tid] / S) : 0u;
       absmax_q[b] = (uint8_t)q8;
     }
     if (tid == 0) absmax_s2[group] = S;
   } else if (absmax_q) {
-    const int64_t b = group * kGroup + tid;
-    if (b < nblocks) {
+    if (tid < kGroup && b < nblocks) {
       uint32_t q8 = 0;
       if (s2 > 0.0f) {
         const float ratio = s_blockmax[tid] / s2;   // IEEE division
@@ -129,8 +149,7 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
     if (tid == 0) absmax_s2[group] = s2;
   } else {
     // no double quantization: the float32 block constants themselves
-    const int64_t b = group * kGroup + tid;
-    if (b < nblocks) absmax_s2[b] = s_blockmax[tid];
+    if (tid < kGroup && b < nblocks) absmax_s2[b] = s_blockmax[tid];
   }
 
   // first level: codes against the exact float32 block maximum
@@ -161,23 +180,23 @@ nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t numel,
         n[2 * i + 1] = bf16_hi(vals[r][i]) / c;
       }
     }
+    // every lane looks up all 8 codes (all table reads in flight
+    // together); a block whose constant is not positive (all zeros) takes
+    // the code of level 0 throughout, and nibbles past the end of the
+    // tensor stay 0
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = bin_code<kFP4>(n[i], s_bins);
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t qa = (c > 0.0f) ? level_rank<kFP4>(n[2 * i], s_thr) : kZeroCode;
-      uint32_t qb = (c > 0.0f) ? level_rank<kFP4>(n[2 * i + 1], s_thr) : kZeroCode;
-      if (kFP4 && c > 0.0f) {
-        qa = s_code[qa];
-        qb = s_code[qb];
-      }
-      // nibbles past the end of the tensor stay 0
-      if (e0 + 2 * i >= numel) qa = 0u;
-      if (e0 + 2 * i + 1 >= numel) qb = 0u;
-      word |= (qa | (qb << 4)) << (8 * i);
-    }
+    for (int i = 0; i < 8; ++i) word |= q[i] << (4 * i);
+    if (!(c > 0.0f)) word = kZeroCode * 0x11111111u;
+    const int64_t rem = numel - e0;
+    if (rem < 8) word &= (1u << (4 * (int)rem)) - 1u;
     const int64_t byte0 = e0 / 2;
     if (byte0 + 4 <= nbytes) {
-      *reinterpret_cast<uint32_t*>(codes + byte0) = word;
+      // streamed out: nothing reads the codes back in this launch
+      __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(codes + byte0));
     } else {
       for (int i = 0; i < 4; ++i)
         if (byte0 + i < nbytes) codes[byte0 + i] = (uint8_t)(word >> (8 * i));
