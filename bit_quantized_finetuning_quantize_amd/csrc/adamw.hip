@@ -17,7 +17,11 @@
 //   p2 = p1 - fl(lr * fl(fl(m1 / c1) / den))  c1 = fl(1 - b1^t)
 // and optionally the bf16 copy of p2 (round to nearest even) that the
 // linear calls take as A or B. The host constants are computed in float64
-// and rounded once. The state may be device memory or pinned host memory
+// and rounded once. The divisions by c1 and c2 (and, for the 8-bit state,
+// by the block scales) are taken as float64 products with the float64
+// reciprocal, rounded once to float32, which gives the correctly rounded
+// quotient (div_rc below); the division by den and the square root are
+// float32's own correctly rounded operations. The state may be device memory or pinned host memory
 // mapped into the device's address space: the kernel streams through it in
 // place either way.
 #include <cmath>
@@ -31,7 +35,20 @@ namespace {
 
 struct AdamWConst {
   float lr, lw, b1, ob1, b2, ob2, c1, c2, eps;
+  double rc1, rc2;  // fl64(1 / c1), fl64(1 / c2)
 };
+
+// fl32(x / c) from rc = fl64(1 / c): fl32(fl64(x * rc)). Exact for every
+// float32 x and positive float32 c. A quotient of two float32 values is never
+// a midpoint between adjacent float32 values (a midpoint needs 25 significant
+// bits, and A = M * B with A < 2^24, M >= 2^24 odd has no solution), and its
+// distance from every midpoint is at least 1 / (M * B) > 2^-49 relative; the
+// float64 product is within 2^-52 relative of the quotient, so it rounds to
+// the same float32. Subnormal quotients only widen the margin; 0, infinities
+// and NaN pass through as the division gives them.
+__device__ __forceinline__ float div_rc(float x, double rc) {
+  return (float)((double)x * rc);
+}
 
 __device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g,
                                           const AdamWConst& k) {
@@ -39,8 +56,8 @@ __device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g,
   const float p1 = p - k.lw * p;
   const float m1 = k.b1 * m + k.ob1 * g;
   const float v1 = k.b2 * v + k.ob2 * (g * g);
-  const float den = __builtin_sqrtf(v1 / k.c2) + k.eps;
-  p = p1 - k.lr * ((m1 / k.c1) / den);
+  const float den = __builtin_sqrtf(div_rc(v1, k.rc2)) + k.eps;
+  p = p1 - k.lr * (div_rc(m1, k.rc1) / den);
   m = m1;
   v = v1;
 }
@@ -106,12 +123,44 @@ adamw_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v
 //   code = enc(fl(x / scale)) (0 when scale = 0), top = 448 / 57344,
 // enc rounding to nearest, ties to the even code, saturating at top. One
 // wave owns one block: four parameters per lane, the block maxima by a
-// wave-wide reduction. The parameter, gradient and code accesses are
-// non-temporal: each byte is read and written once per step.
-
-// ofp8_decode / ofp8_encode (common.h) hold the OFP8 conversions.
+// wave-wide reduction, so the new scales are uniform over the wave and
+// x / scale is a product with one float64 reciprocal per wave. The
+// parameter, gradient and code accesses are non-temporal: each byte is read
+// and written once per step.
 
 constexpr int kBlock8 = 256;
+
+// gfx950's OFP8 conversions: v_cvt_f32_fp8 / v_cvt_f32_bf8 decode one byte
+// exactly; v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 encode two floats with
+// rounding to nearest, ties to even, on the subnormal grid below the
+// smallest normal. Inputs are first clamped to the largest finite magnitude
+// (448 / 57344), which makes them saturate like the encoding above. Checked
+// on gfx950 against the bit-level ofp8_encode / ofp8_decode for every
+// non-NaN float32 and every non-NaN code: no difference. (A NaN, which only a
+// NaN gradient brings, is not coded the same way.)
+template <int kSel>
+__device__ __forceinline__ float fp8_sel(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, kSel);
+}
+__device__ __forceinline__ float fp8_byte(uint32_t w, int j) {
+  return j == 0 ? fp8_sel<0>(w) : j == 1 ? fp8_sel<1>(w) : j == 2 ? fp8_sel<2>(w) : fp8_sel<3>(w);
+}
+template <int kSel>
+__device__ __forceinline__ float bf8_sel(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_bf8((int)w, kSel);
+}
+__device__ __forceinline__ float bf8_byte(uint32_t w, int j) {
+  return j == 0 ? bf8_sel<0>(w) : j == 1 ? bf8_sel<1>(w) : j == 2 ? bf8_sel<2>(w) : bf8_sel<3>(w);
+}
+__device__ __forceinline__ float clampf(float x, float t) { return fminf(fmaxf(x, -t), t); }
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, 448.0f), clampf(b, 448.0f), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clampf(c, 448.0f), clampf(d, 448.0f), lo, true);
+}
+__device__ __forceinline__ uint32_t bf8_pack4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(clampf(a, 57344.0f), clampf(b, 57344.0f), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(clampf(c, 57344.0f), clampf(d, 57344.0f), lo, true);
+}
 
 template <bool kVec>
 __global__ void __launch_bounds__(256)
@@ -153,8 +202,8 @@ adamw8_kernel(float* __restrict__ p, uint8_t* __restrict__ m8, float* __restrict
     float am = 0.0f, av = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float m = ofp8_decode<4, 3, 7>((mc >> (8 * j)) & 0xffu) * smv;
-      float v = ofp8_decode<5, 2, 15>((vc >> (8 * j)) & 0xffu) * svv;
+      float m = fp8_byte(mc, j) * smv;
+      float v = bf8_byte(vc, j) * svv;
       adamw_one(pv[j], m, v, gv[j], k);
       mv[j] = m;
       vv[j] = v;
@@ -170,13 +219,15 @@ adamw8_kernel(float* __restrict__ p, uint8_t* __restrict__ m8, float* __restrict
     }
     const float smn = am / 448.0f;      // IEEE division
     const float svn = av / 57344.0f;
+    // the scales are the same for the whole wave: one float64 reciprocal each
     uint32_t mo = 0, vo = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t cm = smn != 0.0f ? ofp8_encode<4, 3, 7, 0x7Eu>(mv[j] / smn) : 0u;
-      const uint32_t cv = svn != 0.0f ? ofp8_encode<5, 2, 15, 0x7Bu>(vv[j] / svn) : 0u;
-      mo |= cm << (8 * j);
-      vo |= cv << (8 * j);
+    if (smn != 0.0f) {
+      const double r = 1.0 / (double)smn;
+      mo = fp8_pack4(div_rc(mv[0], r), div_rc(mv[1], r), div_rc(mv[2], r), div_rc(mv[3], r));
+    }
+    if (svn != 0.0f) {
+      const double r = 1.0 / (double)svn;
+      vo = bf8_pack4(div_rc(vv[0], r), div_rc(vv[1], r), div_rc(vv[2], r), div_rc(vv[3], r));
     }
     if (kVec && whole) {
       __builtin_nontemporal_store(floatx4{pv[0], pv[1], pv[2], pv[3]}, reinterpret_cast<floatx4*>(p + e0));
@@ -213,6 +264,8 @@ AdamWConst adamw_const(float lr, float beta1, float beta2, float eps, float weig
   k.c1 = (float)(1.0 - std::pow((double)beta1, (double)step));
   k.c2 = (float)(1.0 - std::pow((double)beta2, (double)step));
   k.eps = eps;
+  k.rc1 = 1.0 / (double)k.c1;
+  k.rc2 = 1.0 / (double)k.c2;
   return k;
 }
 
