@@ -40,10 +40,11 @@ def log(*a):
 # of `bench.py --pmc-pass` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for a plain elementwise kernel of known size, and
 # is reported only while the kernel's sources are the ones it was taken on.
-PMC_FILE = os.path.join(ROOT, "profiles", "fwd_contraction_pmc.json")
-KERNEL_SOURCES = ["common.h", "gemm.h", "linear.hip"]
+PMC_FILE = os.path.join(ROOT, "profiles", "nf4_linear_traffic_pmc.json")
+KERNEL_SOURCES = ["common.h", "gemm.h", "linear.hip", "gemv.hip"]
 CALIB_ELEMS = 64 << 20  # float32 in and out: 256 MiB read, 256 MiB written
 PMC_SHAPE = dict(M=2048, N=11008, K=4096, r=64, alpha=16)
+GEMV_PMC_SHAPE = dict(M=1, N=4096, K=4096, r=16, alpha=32, stores=64)
 
 
 def kernel_source_hash():
@@ -73,7 +74,9 @@ def fwd_algorithmic_bytes(M, N, K, r, **_):
 def pmc_pass():
     """The dispatches the counter runs read: three calibration kernels, then
     three forward and three backward passes of the gate projection (the
-    contractions are launches of each)."""
+    contractions are launches of each), then the decode GEMV (M = 1) once on
+    each of 64 weight stores, so that every call reads its store from
+    beyond the last-level cache."""
     import torch
     import bit_quantized_finetuning_quantize_amd as q
     import synthetic
@@ -83,6 +86,7 @@ def pmc_pass():
     for _ in range(3):
         torch.mul(a, 2.0, out=b)
     torch.cuda.synchronize()
+    del a, b
     sh = PMC_SHAPE
     W, X, A, B, _ = synthetic.linear_inputs(sh["M"], sh["N"], sh["K"], sh["r"], dev, seed=0,
                                            base=synthetic.linear_base(0, 0))
@@ -94,16 +98,35 @@ def pmc_pass():
     for _ in range(3):
         q.qlora_linear_bwd(dY, X, T, st, A, B, sh["alpha"] / sh["r"], ws=ws)
     torch.cuda.synchronize()
+    del W, X, A, B, st, ws, dY, Y, T
+    g = GEMV_PMC_SHAPE
+    stores = []
+    for i in range(g["stores"]):
+        Wg = synthetic.normal((g["N"], g["K"]), 0.02, dev, 100 + i, synthetic.W_IDX)
+        stores.append(q.qlora_nf4_quantize(Wg))
+        del Wg
+    Ag = synthetic.normal((g["K"], g["r"]), 0.01, dev, 0, synthetic.A_IDX)
+    Bg = synthetic.normal((g["r"], g["N"]), 0.01, dev, 0, synthetic.B_IDX)
+    Xg = synthetic.normal((g["M"], g["K"]), 1.0, dev, 0, synthetic.X_IDX)
+    Yg = torch.empty(g["M"], g["N"], dtype=torch.bfloat16, device=dev)
+    wsg = torch.empty(q.qlora_linear_workspace_bytes(g["M"], g["N"], g["K"], g["r"]),
+                      dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for stg in stores:
+        q.qlora_linear_fwd(Xg, stg, Ag, Bg, g["alpha"] / g["r"], want_T=False, Y=Yg, ws=wsg)
+    torch.cuda.synchronize()
     log("[pmc] done")
 
 
 def _pmc_values(d, counter):
+    """Median counter value per dispatch of each kernel the pass launches:
+    the calibration kernel, the forward and dX contractions, the GEMV."""
     import csv
     import glob
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {d}")
-    calib, fwd = [], []
+    vals = {"calib": [], "fwd": [], "dx": [], "gemv": [], "gemv_lowrank": []}
     for fn in files:
         with open(fn) as fh:
             for row in csv.DictReader(fh):
@@ -112,24 +135,56 @@ def _pmc_values(d, counter):
                 name = row.get("Kernel_Name", "")
                 v = float(row["Counter_Value"])
                 if "contraction_kernel" in name and "Nf4Rows" in name:
-                    fwd.append(v)
+                    vals["fwd"].append(v)
+                elif "contraction_kernel" in name and "Nf4Cols" in name:
+                    vals["dx"].append(v)
+                elif "nf4_gemv_kernel" in name:
+                    vals["gemv"].append(v)
+                elif "nf4_lowrank_kernel" in name:
+                    vals["gemv_lowrank"].append(v)
                 elif "MulFunctor" in name and row.get("Grid_Size") == str(CALIB_ELEMS // 4):
-                    calib.append(v)  # the calibration kernel: 4 floats per work-item
-    if len(calib) < 1 or len(fwd) < 1:
-        raise SystemExit(f"{counter}: calibration dispatches {len(calib)}, forward {len(fwd)}")
+                    vals["calib"].append(v)  # the calibration kernel: 4 floats per work-item
+    for k, v in vals.items():
+        if not v:
+            raise SystemExit(f"{counter}: no {k} dispatches")
     med = lambda x: sorted(x)[len(x) // 2]
-    return med(calib), med(fwd), len(calib), len(fwd)
+    return {k: (med(v), len(v)) for k, v in vals.items()}
+
+
+def dx_algorithmic_bytes(M, N, K, r, **_):
+    """Bytes the dX contraction must move once: dY, the NF4 store, s*G (bf16,
+    rank padded to 64), the adapter A, and dX."""
+    r64 = (r + 63) // 64 * 64
+    nb = N * K // 64
+    return (2 * M * N + N * K // 2 + nb + (nb + 255) // 256 * 4 + 2 * M * r64 + 2 * r * K
+            + 2 * M * K)
+
+
+def gemv_weight_bytes(N, K, **_):
+    nb = N * K // 64
+    return N * K // 2 + nb + (nb + 255) // 256 * 4
 
 
 def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
-    cf, ff, ncf, nff = _pmc_values(fetch_dir, "FETCH_SIZE")
-    cw, fw, ncw, nfw = _pmc_values(write_dir, "WRITE_SIZE")
+    vf = _pmc_values(fetch_dir, "FETCH_SIZE")
+    vw = _pmc_values(write_dir, "WRITE_SIZE")
     calib_bytes = 4 * CALIB_ELEMS
-    k_fetch = cf * 1024 / calib_bytes   # counter bytes per true byte
-    k_write = cw * 1024 / calib_bytes
-    fetch = ff * 1024 / k_fetch
-    write = fw * 1024 / k_write
-    alg = fwd_algorithmic_bytes(**PMC_SHAPE)
+    k_fetch = vf["calib"][0] * 1024 / calib_bytes   # counter bytes per true byte
+    k_write = vw["calib"][0] * 1024 / calib_bytes
+
+    def entry(key, alg):
+        fetch = vf[key][0] * 1024 / k_fetch
+        write = vw[key][0] * 1024 / k_write
+        e = {"FETCH_SIZE_KiB": vf[key][0], "WRITE_SIZE_KiB": vw[key][0],
+             "dispatches": [vf[key][1], vw[key][1]],
+             "fetch_bytes": round(fetch), "write_bytes": round(write),
+             "traffic_bytes": round(fetch + write)}
+        if alg:
+            e["algorithmic_bytes"] = alg
+            e["traffic_over_algorithmic"] = round((fetch + write) / alg, 3)
+        return e
+
+    g = GEMV_PMC_SHAPE
     out = {
         "kernel": "contraction_kernel (NF4 forward: DirectRows<256>, Nf4Rows<128> + LoRA segment)",
         "workload": "gate projection W 11008x4096 NF4, X 2048x4096 bf16, r=64",
@@ -137,13 +192,15 @@ def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "sources": KERNEL_SOURCES,
         "calibration": {"kernel": "torch.mul(float32[64Mi], 2.0, out=float32[64Mi])",
                         "bytes_read": calib_bytes, "bytes_written": calib_bytes,
-                        "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                        "FETCH_SIZE_KiB": vf["calib"][0], "WRITE_SIZE_KiB": vw["calib"][0],
                         "fetch_factor": round(k_fetch, 4), "write_factor": round(k_write, 4),
-                        "dispatches": [ncf, ncw]},
-        "forward": {"FETCH_SIZE_KiB": ff, "WRITE_SIZE_KiB": fw, "dispatches": [nff, nfw],
-                    "fetch_bytes": round(fetch), "write_bytes": round(write),
-                    "traffic_bytes": round(fetch + write), "algorithmic_bytes": alg,
-                    "traffic_over_algorithmic": round((fetch + write) / alg, 3)},
+                        "dispatches": [vf["calib"][1], vw["calib"][1]]},
+        "forward": entry("fwd", fwd_algorithmic_bytes(**PMC_SHAPE)),
+        "dx": entry("dx", dx_algorithmic_bytes(**PMC_SHAPE)),
+        "gemv": dict(entry("gemv", None), workload="decode GEMV W 4096x4096 NF4, M=1, r=16, "
+                     "one call on each of 64 stores", weight_bytes=gemv_weight_bytes(**g)),
+        "gemv_lowrank": dict(entry("gemv_lowrank", None),
+                             what="the T = X A partials launch of the same calls"),
         "commands": [cmd_fetch, cmd_write],
     }
     os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
@@ -152,8 +209,9 @@ def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
     print(json.dumps(out, indent=1))
 
 
-def stored_traffic():
-    """(bytes per launch, detail) of the forward contraction, or (None, why)."""
+def stored_counters():
+    """The stored counter summary, or (None, why) when there is none or the
+    kernel sources changed since it was taken."""
     try:
         with open(PMC_FILE) as fh:
             d = json.load(fh)
@@ -161,6 +219,14 @@ def stored_traffic():
         return None, "no counter summary"
     if d.get("source_hash") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
+    return d, None
+
+
+def stored_traffic():
+    """(bytes per launch, detail) of the forward contraction, or (None, why)."""
+    d, why = stored_counters()
+    if d is None:
+        return None, why
     f = d["forward"]
     return f["traffic_bytes"], {"fetch_bytes": f["fetch_bytes"], "write_bytes": f["write_bytes"],
                                 "algorithmic_bytes": f["algorithmic_bytes"],
@@ -862,6 +928,12 @@ def main():
         log(f"[bench] cpu {cpu['value']:.4f} TFLOP/s")
     ev.close()
     traffic, traffic_detail = stored_traffic()
+    counters, _ = stored_counters()
+    dx_traffic = counters["dx"]["traffic_bytes"] if counters and "dx" in counters else None
+    if gemv is not None and counters and "gemv" in counters:
+        # HBM bytes of the GEMV launch and of the T partials launch of a call
+        gemv["M1"]["roofline"]["traffic"] = (counters["gemv"]["traffic_bytes"]
+                                             + counters["gemv_lowrank"]["traffic_bytes"])
 
     line = {
         "metric": METRIC,
@@ -900,6 +972,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(pre["dx_kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(pre["dx_kernel_ms"], 4),
+            "traffic": dx_traffic,
         },
         "prefill_kernels_ms": {"fwd": [round(x, 4) for x in pre["per_proj_fwd_ms"]],
                                "dx": [round(x, 4) for x in pre["per_proj_dx_ms"]],
