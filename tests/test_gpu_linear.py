@@ -74,6 +74,22 @@ def test_decode_gemv_down_projection(q, M):
 
 
 @pytest.mark.parametrize("shape", [
+    (1, 256, 640, 6),         # short adapter rows (6 ranks)
+    (1, 256, 640, 3),         # an odd rank: adapter rows off a 4-byte boundary
+    (2, 192, 4160, 16),       # a second, partial 4096-wide pass
+    (3, 320, 64, 8),          # one block of K
+    (4, 128, 8256, 13),       # three passes, the last one partial, odd rank
+])
+@pytest.mark.parametrize("zero", [None, "W"])
+def test_decode_small_ranks(q, shape, zero):
+    """The small-M path at M <= 4 with ranks below 16 and K over partial
+    4096-wide passes; with W = 0, Y is the adapter term alone."""
+    M, N, K, r = shape
+    _run(q, M, N, K, r, 2 * r, seed=M * 7 + r, bwd=False, zero=zero,
+         label=f"small-M M={M} N={N} K={K} r={r}" + (" W=0" if zero else ""))
+
+
+@pytest.mark.parametrize("shape", [
     (17, 256, 256, 8),        # just above the GEMV limit
     (300, 320, 192, 16),      # ragged M, N not a multiple of 128, K % 128 = 64
     (256, 128, 128, 64),      # exactly one tile
