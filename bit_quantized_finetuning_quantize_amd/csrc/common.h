@@ -228,24 +228,6 @@ __device__ __forceinline__ float level_hi(const float* lv16, CodeOffsets o, int 
                                          ((o.hi16 >> (8 * j)) & 0xffu));
 }
 
-// The 32 levels of a 16-byte packet of codes, all lookups issued before any
-// use so that one LDS round trip covers them (the empty asm with a memory
-// clobber keeps the compiler from interleaving each lookup with its use).
-// lo[4 w + j] / hi[4 w + j]: the low / high nibble of byte j of word w.
-__device__ __forceinline__ void packet_levels(const u32x4& c, const float* lv, const float* lv16,
-                                              float (&lo)[16], float (&hi)[16]) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const CodeOffsets o = code_offsets(c[w]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo[4 * w + j] = level_lo(lv, o, j);
-      hi[4 * w + j] = level_hi(lv16, o, j);
-    }
-  }
-  asm volatile("" ::: "memory");
-}
-
 // Lookups without LDS, for one block constant cs and the 16 levels lv of
 // the store type (in code order). The 16 possible weights
 // bf16(fl32(L[q] * cs)) are computed once (16 multiplies, the same two
@@ -278,7 +260,8 @@ __device__ __forceinline__ uint32_t perm_lookup(const uint32_t (&p)[4], uint32_t
   const uint32_t b = __builtin_amdgcn_perm(p[3], p[2], sel);
   return (b & mask) | (a & ~mask);
 }
-// 8 codes -> 4 words of bf16 pairs, bit-identical to dequant_word8.
+// 8 codes -> 4 words of bf16 pairs bf16(fl32(L[q] * cs)) (the two roundings
+// happen once per table entry, in perm_table).
 __device__ __forceinline__ u32x4 dequant_word_perm(uint32_t w, const PermTable& t) {
   // byte masks from bit 3 of each code: v_perm selector 8 (9, 10, 11) copies
   // bit 7 of byte 1 (3, 5, 7) of its source pair into a whole byte
@@ -320,18 +303,6 @@ __device__ __forceinline__ u32x4 dequant_word_perm_oddeven(uint32_t w, const Per
 __device__ __forceinline__ u32x4 x_order_oddeven(const u32x4& v) {
   return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
                __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
-}
-
-// 8 codes -> 4 words of bf16 pairs bf16(fl32(L[q] * cs)): two roundings,
-// never fused.
-__device__ __forceinline__ u32x4 dequant_word8(uint32_t word, float cs, const float* lv,
-                                               const float* lv16) {
-#pragma clang fp contract(off)
-  const CodeOffsets o = code_offsets(word);
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2(level_lo(lv, o, j) * cs, level_hi(lv16, o, j) * cs);
-  return r;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) {

@@ -364,34 +364,38 @@ struct Nf4Rows {
 };
 
 // NF4 weight, transposed (input gradient): tile row i = input feature
-// k0 + i, contraction = output feature n. Producer wave w (= t / 64) owns
-// tile rows 32 w .. 32 w + 31; lane t % 64 owns weight row n = 64 step +
-// t % 64 and loads its 32 codes (one 16-byte packet, inside one 64-block)
-// with one 8-bit constant and one second-level constant. The values are
-// written as 2-byte stores: for each k the 64 lanes of a wave fill one whole
-// 128-byte LDS row, so the transposition costs no bank conflicts.
+// k0 + i, contraction = output feature n. Producer lane t owns the weight
+// rows n = 64 step + 2 (t % 32) and the next one, and input features
+// k0 + 16 (t / 32) .. + 15 (one 8-byte code load per row, inside one
+// 64-block, with the row's 8-bit and second-level constants). For each k
+// the lane writes the two rows' values as one 4-byte store, and the 32 lanes
+// of a half-wave fill one whole 128-byte LDS row, so the transposition costs
+// no bank conflicts.
 template <int R>
 struct Nf4Cols {
   static constexpr bool kWideConsumers = false;
-  static_assert(R == 128, "four producer waves x 32 tile rows");
+  static_assert(R == 128, "eight groups of 16 tile rows");
   static constexpr int kDirect = 0;
-  static constexpr int kRegLoads = 3;
+  static constexpr int kRegLoads = 6;
   const uint8_t* codes;
   const uint8_t* absmax_q;
   const float* absmax_s2;
   int64_t N, K;
   Nf4Consts cst;
-  int vcode, vq;
-  int blk0;  // block index of (row t % 64, this k range) at step 0
-  struct Regs { u32x4 c; uint32_t q8; float s2; };
+  int vcode[2], vq[2];
+  int blk0[2];  // block index of (row 2 (t % 32) + h, this k range) at step 0
+  struct Regs { u32x2 c[2]; uint32_t q8[2]; float s2[2]; };
   __device__ __forceinline__ void setup(int64_t k0, int t) {
-    const int nl = t & 63, kq = t >> 6;
-    const int64_t k = k0 + kq * 32;
+    const int np = t & 31, kq = t >> 5;
+    const int64_t k = k0 + kq * 16;
     const bool ok = k < K;
-    const int64_t e = (int64_t)nl * K + k;
-    vcode = ok ? (int)(e / 2) : 0x7ffffff0;
-    vq = ok ? (int)(e / kBlock) : 0x7ffffff0;
-    blk0 = (int)(e / kBlock);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t e = (int64_t)(2 * np + h) * K + k;
+      vcode[h] = ok ? (int)(e / 2) : 0x7ffffff0;
+      vq[h] = ok ? (int)(e / kBlock) : 0x7ffffff0;
+      blk0[h] = (int)(e / kBlock);
+    }
   }
   __device__ __forceinline__ void direct(int, uint32_t, int) const {}
   __device__ __forceinline__ void load(int step, Regs& r, int) const {
@@ -399,34 +403,42 @@ struct Nf4Cols {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(absmax_q, absmax_q ? (N * K) / kBlock : 0);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(absmax_s2, cst.s2_bytes(N * K / kBlock));
     const int kb = (int)(K / kBlock);
-    r.c = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vcode, step * kStep * (int)(K / 2), 0));
-    r.q8 = __builtin_amdgcn_raw_buffer_load_b8(rq, vq, step * kStep * kb, 0) | cst.q8or;
-    const int g = (blk0 + step * kStep * kb) >> cst.gshift;
-    r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, g * 4, 0, 0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      r.c[h] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, vcode[h], step * kStep * (int)(K / 2), 0));
+      r.q8[h] = __builtin_amdgcn_raw_buffer_load_b8(rq, vq[h], step * kStep * kb, 0) | cst.q8or;
+      const int g = (blk0[h] + step * kStep * kb) >> cst.gshift;
+      r.s2[h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, g * 4, 0, 0));
+    }
   }
   __device__ __forceinline__ void store(const Regs& r, uint32_t tile, const Tables& tb, int t) const {
 #pragma clang fp contract(off)
-    // level lookups from LDS: this producer is bound by its 2-byte
-    // transposing stores, and the input-gradient consumers leave LDS
-    // bandwidth to spare
-    const int nl = t & 63, kq = t >> 6;
-    const float l8 = tb.l8[r.q8];
-    float lo[16], hi[16];
-    packet_levels(r.c, tb.lv, tb.lv16, lo, hi);
-    const float cs = l8 * r.s2;
-    const uint32_t col = (uint32_t)((nl & 7) * 2);
+    // level lookups from LDS: this producer is bound by its transposing
+    // stores, and the input-gradient consumers leave LDS bandwidth to spare;
+    // all 32 lookups are issued before any use (one LDS round trip)
+    const int np = t & 31, kq = t >> 5;
+    float lv[2][16];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t pk = pack_bf16x2(lo[4 * w + j] * cs, hi[4 * w + j] * cs);
-        const int row = kq * 32 + w * 8 + 2 * j;  // k of the low half
-        const uint32_t a0 = tile + (uint32_t)tile_off(row, nl >> 3) + col;
-        const uint32_t a1 = tile + (uint32_t)tile_off(row + 1, nl >> 3) + col;
-        *(__attribute__((address_space(3))) uint16_t*)(uintptr_t)a0 = (uint16_t)(pk & 0xffffu);
-        *(__attribute__((address_space(3))) uint16_t*)(uintptr_t)a1 = (uint16_t)(pk >> 16);
+      for (int w = 0; w < 2; ++w) {
+        const CodeOffsets o = code_offsets(r.c[h][w]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lv[h][8 * w + 2 * j] = level_lo(tb.lv, o, j);
+          lv[h][8 * w + 2 * j + 1] = level_hi(tb.lv16, o, j);
+        }
       }
+    asm volatile("" ::: "memory");
+    const float cs0 = tb.l8[r.q8[0]] * r.s2[0];
+    const float cs1 = tb.l8[r.q8[1]] * r.s2[1];
+    const uint32_t col = (uint32_t)((np & 3) * 4);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const uint32_t pk = pack_bf16x2(lv[0][kk] * cs0, lv[1][kk] * cs1);
+      const uint32_t a = tile + (uint32_t)tile_off(kq * 16 + kk, np >> 2) + col;
+      *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)a = pk;
     }
   }
 };
