@@ -45,16 +45,27 @@ namespace {
 constexpr int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Number of contraction splits for a split-K launch: about one workgroup per
-// compute unit (measured faster than two: fewer partials to write and sum),
-// at least two steps per split.
+// Number of contraction splits for a split-K launch: at most about one
+// workgroup per compute unit (measured faster than two: fewer partials to
+// write and sum), at least two steps per split, and among those the count
+// whose rounds of 256 workgroups times steps per split is least (ties to
+// fewer splits): 118 tiles over 32 steps take 2 splits (236 workgroups, one
+// round of 16 steps), not 3 (354 workgroups, two rounds of 11).
 int64_t choose_splits(int64_t tiles, int64_t steps) {
-  int64_t want = ceil_div(256, std::max<int64_t>(tiles, 1));
-  int64_t maxs = std::max<int64_t>(1, steps / 2);
-  int64_t s = std::min(want, maxs);
-  if (s < 1) s = 1;
-  const int64_t per = ceil_div(steps, s);
-  return ceil_div(steps, per);
+  tiles = std::max<int64_t>(tiles, 1);
+  const int64_t want = ceil_div(256, tiles);
+  const int64_t maxs = std::max<int64_t>(1, steps / 2);
+  int64_t best = 1, best_cost = ceil_div(tiles, 256) * steps;
+  for (int64_t s = 2; s <= std::min(want, maxs); ++s) {
+    const int64_t per = ceil_div(steps, s);
+    const int64_t sc = ceil_div(steps, per);  // splits actually formed
+    const int64_t cost = ceil_div(tiles * sc, 256) * per;
+    if (cost < best_cost) {
+      best = sc;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // Split count shared by the dA and dB^T contractions of one launch.
