@@ -540,25 +540,30 @@ struct Consumer {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
   // four 16-deep sub-steps; the fragments of sub-step kk+1 are read while
-  // the matrix cores work on sub-step kk
+  // the matrix cores work on sub-step kk. One sub-step ahead, not two: right
+  // after a stage barrier every consumer wave reads its first fragments at
+  // once, and a smaller burst lets the first MFMAs start sooner (same-box
+  // A/B: equal or up to 2 % faster, bit-identical).
   __device__ __forceinline__ void step(uint32_t sA, uint32_t sB) {
     bf16x8 a0[BP], b0[BQ], a1[BP], b1[BQ];
     frags(sA, sB, 0, a0, b0);
+    mma(a0, b0);
     frags(sA, sB, 1, a1, b1);
-    mma(a0, b0);
+    mma(a1, b1);
     frags(sA, sB, 2, a0, b0);
-    mma(a1, b1);
-    frags(sA, sB, 3, a1, b1);
     mma(a0, b0);
+    frags(sA, sB, 3, a1, b1);
     mma(a1, b1);
-    // keep two sub-steps of fragment reads in flight ahead of the MFMAs
+    // the reads of sub-step kk + 1 go out after the first MFMA of kk
     constexpr int kF = BP + BQ, kM = BP * BQ;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF, 0);  // LDS reads, kk = 0, 1
-    __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);      // MFMA kk = 0
-    __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk = 2
-    __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);      // MFMA kk = 1
-    __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk = 3
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kM, 0);  // MFMA kk = 2, 3
+    __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk = 0
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // first MFMA of kk
+      __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);      // LDS reads kk + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, kM - 1, 0);  // rest of kk
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);      // MFMA kk = 3
   }
 
   // Keep bits of this lane's accumulator elements under a dropout mask over
