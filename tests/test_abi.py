@@ -192,6 +192,22 @@ def _merge(lib, N=128, K=128, r=8, codes=FAKE, A=FAKE, out=FAKE, s2=FAKE):
     return lib.qlora_nf4_merge(codes, FAKE, s2, N, K, A, FAKE, r, 0.25, out, None)
 
 
+def test_workspace_serves_smaller_linears(lib):
+    """A workspace sized for a linear serves every linear of the same token
+    count and rank with no larger K and N (the split-K partial buffer is
+    sized by a bound that grows with K and N), so one workspace sized for a
+    model's largest linear serves all of them."""
+    dims = [64, 192, 256, 1024, 4096, 8192, 11008, 22016]
+    for M in (17, 300, 2048, 4096):
+        for r in (8, 64, 100):
+            size = {(N, K): lib.qlora_linear_workspace_bytes(M, N, K, r)
+                    for N in dims for K in dims}
+            for (N, K), b in size.items():
+                for (N2, K2), b2 in size.items():
+                    if N <= N2 and K <= K2:
+                        assert b <= b2, (M, r, N, K, N2, K2, b, b2)
+
+
 def test_merge_rejects(lib):
     assert _merge(lib, codes=None) == -1
     assert _merge(lib, A=None) == -1
