@@ -369,8 +369,8 @@ struct Nf4Rows {
 // k0 + 16 (t / 32) .. + 15 (one 8-byte code load per row, inside one
 // 64-block, with the row's 8-bit and second-level constants). For each k
 // the lane writes the two rows' values as one 4-byte store, and the 32 lanes
-// of a half-wave fill one whole 128-byte LDS row, so the transposition costs
-// no bank conflicts.
+// of a half-wave fill one whole 128-byte LDS row: 16 stores per lane and
+// step, each without bank conflicts inside a half-wave.
 template <int R>
 struct Nf4Cols {
   static constexpr bool kWideConsumers = false;
