@@ -126,7 +126,7 @@ def _pmc_values(d, counter):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {d}")
-    vals = {"calib": [], "fwd": [], "dx": [], "gemv": [], "gemv_lowrank": []}
+    vals = {"calib": [], "fwd": [], "dx": [], "gemv": []}
     for fn in files:
         with open(fn) as fh:
             for row in csv.DictReader(fh):
@@ -140,8 +140,6 @@ def _pmc_values(d, counter):
                     vals["dx"].append(v)
                 elif "nf4_gemv_kernel" in name:
                     vals["gemv"].append(v)
-                elif "nf4_lowrank_kernel" in name:
-                    vals["gemv_lowrank"].append(v)
                 elif "MulFunctor" in name and row.get("Grid_Size") == str(CALIB_ELEMS // 4):
                     vals["calib"].append(v)  # the calibration kernel: 4 floats per work-item
     for k, v in vals.items():
@@ -198,9 +196,8 @@ def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "forward": entry("fwd", fwd_algorithmic_bytes(**PMC_SHAPE)),
         "dx": entry("dx", dx_algorithmic_bytes(**PMC_SHAPE)),
         "gemv": dict(entry("gemv", None), workload="decode GEMV W 4096x4096 NF4, M=1, r=16, "
-                     "one call on each of 64 stores", weight_bytes=gemv_weight_bytes(**g)),
-        "gemv_lowrank": dict(entry("gemv_lowrank", None),
-                             what="the T = X A partials launch of the same calls"),
+                     "one call (one launch) on each of 64 stores",
+                     weight_bytes=gemv_weight_bytes(**g)),
         "commands": [cmd_fetch, cmd_write],
     }
     os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
@@ -579,7 +576,7 @@ def run_prefill(args, q, synthetic, torch, dev, ev):
 def run_gemv(args, q, synthetic, torch, dev):
     """Decode GEMV per call, timed by replaying a HIP graph of `nstores`
     back-to-back calls (each on a different weight store), so that host
-    launch overhead is not counted; a call is both of its launches."""
+    launch overhead is not counted; a call is one launch."""
     N = K = 4096
     r, alpha = 16, 32
     s = alpha / r
@@ -628,7 +625,8 @@ def run_gemv(args, q, synthetic, torch, dev):
                             roofline={"bound": "hbm", "achieved": round(gbps, 1),
                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                       "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                                      "per": "call (T partials launch + fused GEMV launch)"})
+                                      "per": "call (one launch: the T = X A workgroups and the "
+                                              "row-tile workgroups)"})
         log(f"[gemv] M={M}: {call_us:.2f} us/call, {gbps:.0f} GB/s effective weight")
     # context for the per-call figures: one vectorized torch elementwise
     # launch that reads the same number of bytes (an int64 view, compared
@@ -931,9 +929,8 @@ def main():
     counters, _ = stored_counters()
     dx_traffic = counters["dx"]["traffic_bytes"] if counters and "dx" in counters else None
     if gemv is not None and counters and "gemv" in counters:
-        # HBM bytes of the GEMV launch and of the T partials launch of a call
-        gemv["M1"]["roofline"]["traffic"] = (counters["gemv"]["traffic_bytes"]
-                                             + counters["gemv_lowrank"]["traffic_bytes"])
+        # HBM bytes of a call's one launch
+        gemv["M1"]["roofline"]["traffic"] = counters["gemv"]["traffic_bytes"]
 
     line = {
         "metric": METRIC,

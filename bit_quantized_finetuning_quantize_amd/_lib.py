@@ -64,6 +64,7 @@ SIGNATURES = {
     "qlora_linear_bwd_profiled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
                                            _c_i64, _c_i32, _c_f32, _vp, _vp, _vp, _vp, _c_size,
                                            _vp, _vp, _vp]),
+    "qlora_gemv_wait_limit": (_c_int, [_c_i64]),
     "qlora_status_string": (ctypes.c_char_p, [_c_int]),
     "qlora_last_hip_error": (_c_int, []),
 }

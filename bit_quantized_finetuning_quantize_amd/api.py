@@ -227,6 +227,10 @@ def qlora_linear_workspace_bytes(M, N, K, r):
     return int(LIB.qlora_linear_workspace_bytes(M, N, K, r))
 
 
+def qlora_gemv_wait_limit(microseconds):
+    _check(LIB.qlora_gemv_wait_limit(int(microseconds)))
+
+
 def workspace(M, N, K, r, device):
     n = qlora_linear_workspace_bytes(M, N, K, r)
     if n == 0:

@@ -382,6 +382,12 @@ int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* X, const float*
                                       dr));
 }
 
+int qlora_gemv_wait_limit(int64_t microseconds) {
+  if (microseconds < 0 || microseconds > 1000000) return QLORA_ERR_INVALID_ARG;
+  qlora::set_gemv_wait_us(microseconds);
+  return QLORA_OK;
+}
+
 const char* qlora_status_string(int status) {
   switch (status) {
     case QLORA_OK: return "ok";

@@ -71,10 +71,12 @@ struct Dropout {
 // Workspace carve-up for the forward and backward of one linear call.
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
-// Small-M forward (M <= kGemvMaxM): split partials of T = X A, then one
-// GEMV launch over row tiles of the whole K that adds s T B and writes Y.
+// Small-M forward (M <= kGemvMaxM): one launch; workgroups that form split
+// partials of T = X A (a copy per XCD), and workgroups over row tiles of the
+// whole K that wait for them, add s T B and write Y.
 constexpr int kGemvMaxM = 16;
 int64_t gemv_partial_elems(int64_t M, int64_t N, int64_t K, int r);
+void set_gemv_wait_us(int64_t us);
 hipError_t launch_fwd_gemv(const uint16_t* X, Nf4Weight W, const uint16_t* A,
                            const uint16_t* B, int M, int64_t N, int64_t K, int r,
                            float scale, uint16_t* Y, float* T_out, void* ws,

@@ -293,9 +293,11 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  *   T_out    device float [M x r]  optional output: T = X A (for the
  *                                  backward); NULL to skip
  * Products of bf16 values accumulate in float32. M <= 16 takes a
- * memory-bound GEMV path (two launches: split partials of X A, then one
- * kernel per 16 weight rows over the whole K that adds the adapter term and
- * writes Y); larger M takes an MFMA GEMM path. Calls capture into a HIP graph (no memset, no allocation).
+ * memory-bound GEMV path (one launch: workgroups that form split partials
+ * of X A, and one workgroup per 16 weight rows over the whole K that waits
+ * for them, adds the adapter term and writes Y; see qlora_gemv_wait_limit);
+ * larger M takes an MFMA GEMM path. Calls capture into a HIP graph (no
+ * memset, no allocation).
  * Errors: INVALID_ARG (null X/codes/absmax/A/B/Y, non-positive M, N, K);
  * UNSUPPORTED (K or N not a multiple of 64, r outside [1, 256], M above
  * 2^30, N or K above 2^21, M N or M K at or above 2^30, N K at or above
@@ -465,6 +467,16 @@ int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* X, const float*
                              int32_t r, float scale, const uint32_t* keep_mask, float p,
                              uint16_t* dX, float* dA, float* dB, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* qlora_gemv_wait_limit — how long, in microseconds, the row-tile
+ * workgroups of a small-M forward (M <= 16) wait for the workgroups of the
+ * same launch that form T = X A, before forming T themselves; the default,
+ * 200, is far beyond the few microseconds those take. 0: no T workgroups
+ * are launched and every row-tile workgroup forms T itself (slower, the
+ * same results bit for bit). Host state shared by all threads; applies to
+ * calls issued after it returns. Errors: INVALID_ARG for a value below 0 or
+ * above 1000000. */
+int qlora_gemv_wait_limit(int64_t microseconds);
 
 /* ---- diagnostics ------------------------------------------------------------ */
 

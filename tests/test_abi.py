@@ -66,6 +66,14 @@ def test_status_strings(lib):
         assert isinstance(lib.qlora_status_string(s), bytes)
 
 
+def test_gemv_wait_limit_range(lib):
+    assert lib.qlora_gemv_wait_limit(-1) == -1
+    assert lib.qlora_gemv_wait_limit(1000001) == -1
+    assert lib.qlora_gemv_wait_limit(0) == 0
+    assert lib.qlora_gemv_wait_limit(1000000) == 0
+    assert lib.qlora_gemv_wait_limit(200) == 0  # the default, restored
+
+
 FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced
 ODD = ctypes.c_void_p((1 << 20) + 1)  # misaligned
 
