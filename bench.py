@@ -39,21 +39,23 @@ def log(*a):
 # HBM traffic of the forward contraction comes from two rocprofv3 --pmc runs
 # of `bench.py --pmc-pass` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for a plain elementwise kernel of known size, and
-# is reported only while the kernel's sources are the ones it was taken on.
+# is reported only while the kernel's sources are the ones it was taken on
+# (one hash for the contractions' sources, one for the GEMV's).
 PMC_FILE = os.path.join(ROOT, "profiles", "nf4_linear_traffic_pmc.json")
-KERNEL_SOURCES = ["common.h", "gemm.h", "linear.hip", "gemv.hip"]
+KERNEL_SOURCES = ["common.h", "gemm.h", "linear.hip"]
+GEMV_SOURCES = ["common.h", "gemv.hip"]
 CALIB_ELEMS = 64 << 20  # float32 in and out: 256 MiB read, 256 MiB written
 PMC_SHAPE = dict(M=2048, N=11008, K=4096, r=64, alpha=16)
 GEMV_PMC_SHAPE = dict(M=1, N=4096, K=4096, r=16, alpha=32, stores=64)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     """Hash of the kernel sources with comments and blank space removed, so
     that an edit of a comment leaves stored counter data valid."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "bit_quantized_finetuning_quantize_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -188,6 +190,8 @@ def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "workload": "gate projection W 11008x4096 NF4, X 2048x4096 bf16, r=64",
         "source_hash": kernel_source_hash(),
         "sources": KERNEL_SOURCES,
+        "gemv_source_hash": kernel_source_hash(GEMV_SOURCES),
+        "gemv_sources": GEMV_SOURCES,
         "calibration": {"kernel": "torch.mul(float32[64Mi], 2.0, out=float32[64Mi])",
                         "bytes_read": calib_bytes, "bytes_written": calib_bytes,
                         "FETCH_SIZE_KiB": vf["calib"][0], "WRITE_SIZE_KiB": vw["calib"][0],
@@ -206,15 +210,17 @@ def pmc_summarize(fetch_dir, write_dir, cmd_fetch, cmd_write):
     print(json.dumps(out, indent=1))
 
 
-def stored_counters():
+def stored_counters(gemv=False):
     """The stored counter summary, or (None, why) when there is none or the
-    kernel sources changed since it was taken."""
+    sources of the contractions (gemv=False) or of the GEMV (gemv=True)
+    changed since it was taken."""
     try:
         with open(PMC_FILE) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None, "no counter summary"
-    if d.get("source_hash") != kernel_source_hash():
+    key, src = ("gemv_source_hash", GEMV_SOURCES) if gemv else ("source_hash", KERNEL_SOURCES)
+    if d.get(key) != kernel_source_hash(src):
         return None, "kernel changed since the counters were taken"
     return d, None
 
@@ -928,9 +934,10 @@ def main():
     traffic, traffic_detail = stored_traffic()
     counters, _ = stored_counters()
     dx_traffic = counters["dx"]["traffic_bytes"] if counters and "dx" in counters else None
-    if gemv is not None and counters and "gemv" in counters:
+    gcounters, _ = stored_counters(gemv=True)
+    if gemv is not None and gcounters and "gemv" in gcounters:
         # HBM bytes of a call's one launch
-        gemv["M1"]["roofline"]["traffic"] = counters["gemv"]["traffic_bytes"]
+        gemv["M1"]["roofline"]["traffic"] = gcounters["gemv"]["traffic_bytes"]
 
     line = {
         "metric": METRIC,
