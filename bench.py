@@ -627,7 +627,11 @@ def run_gemv(args, q, synthetic, torch, dev):
     for M in (1, 4, 16):
         call_us = call_time(M, stores)
         gbps = wbytes / (call_us * 1e-6) / 1e9
+        # every byte a call must move once: the store, X, A, B and Y
+        tbytes = wbytes + 2 * (M * K + K * r + r * N + M * N)
         out[f"M{M}"] = dict(call_us=round(call_us, 3), eff_weight_GBps=round(gbps, 1),
+                            total_bytes=tbytes,
+                            total_GBps=round(tbytes / (call_us * 1e-6) / 1e9, 1),
                             roofline={"bound": "hbm", "achieved": round(gbps, 1),
                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                       "frac": round(gbps / PEAK_HBM_GBPS, 4),
@@ -683,6 +687,60 @@ def run_gemv(args, q, synthetic, torch, dev):
                           eff_weight_GBps=round(nb / (us1 * 1e-6) / 1e9, 1))
     log(f"[gemv] no double quantization, M=1: {us1:.2f} us/call")
     del stores
+    return out
+
+
+def run_single(args, q, synthetic, torch, dev):
+    """The single small linear (W 256x256 NF4, 16 tokens, r=8, alpha=16):
+    quantize, forward and backward (dX, dA, dB), timed by replaying a HIP
+    graph of 64 back-to-back sequences (every launch of the three calls
+    inside). Launch-bound at this size: reported, not a throughput target."""
+    M, N, K, r, alpha = 16, 256, 256, 8, 16
+    s = alpha / r
+    W, X, A, B, dY = synthetic.linear_inputs(M, N, K, r, dev, seed=0)
+    st = q.qlora_nf4_quantize(W)
+    ws = q.workspace(M, N, K, r, dev)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    T = torch.empty(M, r, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(K, r, dtype=torch.float32, device=dev)
+    dB = torch.empty(r, N, dtype=torch.float32, device=dev)
+    reps = 64
+
+    def seq():
+        q.qlora_nf4_quantize(W, out=st)
+        q.qlora_linear_fwd(X, st, A, B, s, Y=Y, T=T, ws=ws)
+        q.qlora_linear_bwd(dY, X, T, st, A, B, s, dX=dX, dA=dA, dB=dB, ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        seq()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            seq()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / reps
+        best = us if best is None else min(best, us)
+    flops = 4 * M * N * K + 6 * M * r * (K + N)
+    out = dict(workload="single linear W 256x256 NF4 (block 64, DQ 256), X 16x256, r=8 "
+                        "alpha=16: quantize + fwd + bwd (dX, dA, dB)",
+               us_per_sequence=round(best, 3), flops=flops,
+               timing="HIP graph replay of 64 back-to-back sequences, best of 3")
+    log(f"[single] 256x256, 16 tokens: {best:.2f} us per quantize + fwd + bwd")
+    del g
     return out
 
 
@@ -917,9 +975,12 @@ def main():
     log(f"[bench] {pre['tflops']:.1f} TFLOP/s, {pre['ms_per_step']:.3f} ms/step; fwd kernel "
         f"{pre['fwd_kernel_tflops']:.1f} TFLOP/s, dX kernel {pre['dx_kernel_tflops']:.1f}")
     gemv = None
+    single = None
     if not args.no_gemv:
         log("[bench] decode GEMV ...")
         gemv = run_gemv(args, q, synthetic, torch, dev)
+        log("[bench] single small linear ...")
+        single = run_single(args, q, synthetic, torch, dev)
     stacks = None
     if not args.no_stacks:
         log("[bench] 7B-style stack sweep and 65B-shaped legs ...")
@@ -993,6 +1054,7 @@ def main():
         "dropout": pre["dropout"],
         "nodq": pre["nodq"],
         "gemv": gemv,
+        "single_linear": single,
         "stacks": stacks,
         "cpu_baseline": cpu,
     }
