@@ -672,6 +672,9 @@ def run_gemv(args, q, synthetic, torch, dev):
                                what="torch.ne(int64 view, 0) over the store's bytes, "
                                     "64 rotating buffers, HIP-graph replay")
     log(f"[gemv] streaming floor (torch.ne over {sb} B): {sus:.2f} us per launch")
+    # each call's time against that of the launch that only streams its bytes
+    for M in (1, 4, 16):
+        out[f"M{M}"]["frac_of_stream_floor"] = round(sus / out[f"M{M}"]["call_us"], 4)
     del gs, bufs, flags
     # the same calls on stores without double quantization (float32 block
     # constants, 4.5 bits per weight)
